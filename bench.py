@@ -1,0 +1,246 @@
+"""Benchmark of the target-verify hot path on one MI355X.
+
+One step = one verify of a block: paged causal GQA over the long cache
+(sv_verify_attention: the split attention kernel plus the partial merge) and
+greedy acceptance over the block's fp32 logits (sv_greedy_accept), on seeded
+synthetic inputs already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal]
+
+Prints one JSON line. `value` is the effective HBM bandwidth of the whole step
+(algorithmic bytes of attention + accept / step time). The `roofline` object
+is for the dominant kernel (verify_attn): its algorithmic bytes per launch
+over its average launch duration, measured here with HIP events on the stream
+the kernels run on (the attention call minus the merge kernel, timed
+separately). `cpu_baseline` is the float64 oracle timed on the host on one
+(request, KV head) group of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn effective HBM GB/s (% of peak) at q=8, 512K ctx; verified tok/s"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--variant", default="literal", choices=["literal", "unit"])
+    ap.add_argument("--splits", type=int, default=0, help="force the number of key chunks (0 = planner)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per verify_attn launch (FETCH+WRITE)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the verify path is measured on a "
+                                   "single MI355X; run with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from long_context_gqa_amd import binding as B
+    from long_context_gqa_amd import workloads as W
+
+    B.lib()  # fail loudly if libsv.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.WORKLOADS[args.config]
+    log(f"[bench] workload {wl.name} ({args.variant}): generating inputs on the GPU")
+    t0 = time.time()
+    x = W.make_verify_inputs(wl, args.variant, device=dev)
+    acc_in = W.make_accept_inputs(wl, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s; pool {tuple(x.k_pages.shape)} {x.k_pages.dtype}")
+
+    kv_lens = x.kv_lens.to(dev)
+    page_table = x.page_table.to(dev).contiguous()
+    call = B.VerifyCall(x.q, x.k_pages, x.v_pages, page_table, kv_lens, wl.q_len, x.max_kv_len,
+                        x.k_scales, x.v_scales, x.sm_scale, args.splits)
+    acall = B.AcceptCall(acc_in.logits, acc_in.draft_ids, wl.q_len, kv_lens)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        call.run(stream)
+        acall.run(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    flags = int(call.flags.item())
+    if flags:
+        raise SystemExit(f"kernel flagged a contract violation: {flags}")
+    # sanity of the accept result against the planted lengths (the oracle's
+    # job is in the tests; here only the generator's construction is used)
+    if not torch.equal(acall.accept_len.cpu(), acc_in.planted_accept):
+        raise SystemExit("accept lengths differ from the planted ones")
+
+    # ---- timed region: K whole steps ------------------------------------
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-part timing (same stream, events around each launch) ---------
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs]) * 1e3  # us
+
+    n_part = max(10, args.steps)
+    attn_us = timed(lambda: call.run(stream), n_part)
+    acc_us = timed(lambda: acall.run(stream), n_part)
+    merge_us = np.zeros(1)
+    if call.splits > 1:
+        S, R, Hq, D = call.splits, x.q.shape[0], x.q.shape[1], x.q.shape[2]
+        po_bytes = S * R * Hq * D * 4
+        po = call.workspace[:po_bytes].view(torch.float32).view(S, R, Hq, D)
+        off = (po_bytes + 255) // 256 * 256
+        pl = call.workspace[off:off + S * R * Hq * 4].view(torch.float32).view(S, R, Hq)
+        mout = torch.empty_like(x.q)
+        merge_us = timed(lambda: B.sv_verify_merge(po, pl, mout, None, stream), n_part)
+    kern_us = float(np.median(attn_us) - np.median(merge_us))
+
+    # ---- bytes ----------------------------------------------------------
+    attn_bytes = W.verify_algorithmic_bytes(x.kv_lens.tolist(), wl.q_len, wl.num_q_heads, wl.num_kv_heads,
+                                            wl.head_dim, wl.page_size, wl.kv_dtype)
+    acc_bytes = W.accept_algorithmic_bytes(wl.batch, wl.q_len, wl.vocab)
+    step_s = step_ms * 1e-3
+    value = (attn_bytes + acc_bytes) / step_s / 1e9
+    attn_gbs = attn_bytes / (np.median(attn_us) * 1e-6) / 1e9
+    kern_gbs = attn_bytes / (kern_us * 1e-6) / 1e9
+    rows = wl.batch * wl.q_len
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, wl)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.kv_dtype == "fp16" else "e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "q_len": wl.q_len, "max_kv_len": x.max_kv_len,
+            "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "page_size": wl.page_size, "kv_dtype": wl.kv_dtype, "variant": args.variant,
+            "splits": call.splits, "chunk_tokens": call.chunk,
+        },
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "verify_attention": {
+            "us_median": round(float(np.median(attn_us)), 2),
+            "us_p10": round(float(np.percentile(attn_us, 10)), 2),
+            "us_p90": round(float(np.percentile(attn_us, 90)), 2),
+            "effective_GBps": round(attn_gbs, 1),
+            "pct_of_peak_hbm": round(100 * attn_gbs / PEAK_HBM_GBS, 2),
+            "verified_tok_per_s": round(rows / (np.median(attn_us) * 1e-6), 1),
+            "algorithmic_bytes": attn_bytes,
+            "merge_us_median": round(float(np.median(merge_us)), 2),
+        },
+        "greedy_accept": {
+            "us_median": round(float(np.median(acc_us)), 2),
+            "effective_GBps": round(acc_bytes / (np.median(acc_us) * 1e-6) / 1e9, 1),
+            "algorithmic_bytes": acc_bytes,
+        },
+        "roofline": {
+            "kernel": "verify_attn_f16_kernel",
+            "bound": "hbm",
+            "achieved": round(kern_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "launch_us": round(kern_us, 2),
+            "bytes_per_launch": attn_bytes,
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(x, wl):
+    """The float64 oracle on one (request, KV head) group of the workload:
+    all q_len x G rows over the request's whole cache. Reported in the same
+    unit as the metric (algorithmic bytes of the sample / oracle wall time)."""
+    import numpy as np
+
+    from long_context_gqa_amd import workloads as W
+    from oracle import attention as oatt
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    b, g = 0, 0
+    n = int(x.kv_lens[b])
+    npg = (n + wl.page_size - 1) // wl.page_size
+    log(f"[bench] cpu baseline: oracle on request {b}, KV head {g} ({n} keys)")
+    ids = x.page_table[b, :npg].long().to(x.k_pages.device)
+    # hand the oracle a compact pool holding this request's pages only
+    kp = x.k_pages[ids].cpu()
+    vp = x.v_pages[ids].cpu()
+    ks = x.k_scales[ids].cpu() if x.k_scales is not None else None
+    vs = x.v_scales[ids].cpu() if x.v_scales is not None else None
+    table = np.arange(npg, dtype=np.int32)[None]
+    q = x.q[b * wl.q_len:(b + 1) * wl.q_len].cpu()
+    t0 = time.perf_counter()
+    oatt.verify_attention(q, kp, vp, table, np.array([n]), wl.q_len, x.sm_scale, ks, vs, rows=[(0, g)])
+    dt = time.perf_counter() - t0
+    G = wl.num_q_heads // wl.num_kv_heads
+    sample_bytes = n * W.kv_bytes_per_token_head(wl.head_dim, wl.kv_dtype) + 2 * wl.q_len * G * wl.head_dim * 2
+    return {
+        "value": round(sample_bytes / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"float64 oracle, request 0 KV head 0: {wl.q_len}x{G} rows over {n} keys "
+                  f"({sample_bytes} algorithmic bytes) in {dt:.2f} s; host has {os.cpu_count()} CPUs",
+        "seconds": round(dt, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+// Greedy acceptance of a verify block: block-wise argmax over fp32 logits,
+// then the longest prefix of drafts that match, the bonus token and the new
+// cache length.
+//
+// Stage 1 (argmax_partial): one workgroup per (row, slice of the vocabulary);
+//   every thread walks its float4 columns in increasing order, so the
+//   per-thread winner already prefers the lowest index; winners are combined
+//   with the rule "larger value, then lower index" across the wave (shuffles)
+//   and across the 4 waves (LDS). Output (value, index) per (row, slice).
+// Stage 2 (accept_finalize): one wave per request combines the slices of its
+//   q_len rows with the same rule and walks the drafts.
+// The logits are read once; the scan is HBM-bound.
+#include <stdint.h>
+
+#include "sv_common.h"
+#include "sv_accept.h"
+
+namespace sv {
+
+namespace {
+
+struct Best {
+  float v;
+  int i;
+};
+
+__device__ __forceinline__ Best better(Best a, Best b) {
+  // larger value wins; equal values: lower index wins. NaN never wins.
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+__device__ __forceinline__ Best wave_best(Best x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Best y;
+    y.v = __shfl_xor(x.v, o);
+    y.i = __shfl_xor(x.i, o);
+    x = better(x, y);
+  }
+  return x;
+}
+
+}  // namespace
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* __restrict__ logits,
+                                                                  int vocab, int slice,
+                                                                  int n_slices, float2* ws) {
+  const int sl = blockIdx.x, row = blockIdx.y;
+  const int lo = sl * slice, hi = min(lo + slice, vocab);
+  const float* rp = logits + (size_t)row * vocab;
+  Best b{-INFINITY, INT32_MAX};
+  if (VEC4) {
+    // columns [lo, hi) with lo, hi multiples of 4 (vocab % 4 == 0)
+    for (int c = lo + 4 * threadIdx.x; c < hi; c += 4 * kThreads) {
+      const float4 v = *reinterpret_cast<const float4*>(rp + c);
+      b = better(b, Best{v.x, c});
+      b = better(b, Best{v.y, c + 1});
+      b = better(b, Best{v.z, c + 2});
+      b = better(b, Best{v.w, c + 3});
+    }
+  } else {
+    for (int c = lo + threadIdx.x; c < hi; c += kThreads) b = better(b, Best{rp[c], c});
+  }
+  b = wave_best(b);
+  __shared__ Best sb[kWavesPerGroup];
+  const int w = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) sb[w] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Best r = sb[0];
+    for (int k = 1; k < kWavesPerGroup; ++k) r = better(r, sb[k]);
+    ws[(size_t)row * n_slices + sl] = make_float2(r.v, __int_as_float(r.i));
+  }
+}
+
+__global__ __launch_bounds__(kWave) void accept_finalize_kernel(
+    const float2* __restrict__ ws, int n_slices, const int32_t* __restrict__ draft_ids, int q_len,
+    int32_t* accept_len, int32_t* bonus_ids, int32_t* argmax_ids, const int32_t* kv_lens_in,
+    int32_t* kv_lens_out) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  int acc = 0;
+  bool open = true;  // still matching
+  int bonus = 0;
+  for (int j = 0; j < q_len; ++j) {
+    const size_t row = (size_t)b * q_len + j;
+    Best x{-INFINITY, INT32_MAX};
+    for (int s = lane; s < n_slices; s += kWave) {
+      const float2 p = ws[row * n_slices + s];
+      x = better(x, Best{p.x, __float_as_int(p.y)});
+    }
+    x = wave_best(x);
+    const int am = (x.i == INT32_MAX) ? 0 : x.i;
+    if (argmax_ids && lane == 0) argmax_ids[row] = am;
+    if (open) {
+      if (j < q_len - 1 && draft_ids[(size_t)b * (q_len - 1) + j] == am) {
+        ++acc;
+      } else {
+        open = false;
+        bonus = am;
+        if (!argmax_ids) break;
+      }
+    }
+  }
+  if (lane == 0) {
+    accept_len[b] = acc;
+    bonus_ids[b] = bonus;
+    if (kv_lens_out) kv_lens_out[b] = kv_lens_in[b] - q_len + 1 + acc;
+  }
+}
+
+void launch_greedy_accept(const AcceptLaunch& a, hipStream_t s) {
+  dim3 g1(a.n_slices, a.batch * a.q_len);
+  if (a.vocab % 4 == 0)
+    hipLaunchKernelGGL((argmax_partial_kernel<true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
+                       a.slice, a.n_slices, a.ws);
+  else
+    hipLaunchKernelGGL((argmax_partial_kernel<false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
+                       a.slice, a.n_slices, a.ws);
+  hipLaunchKernelGGL(accept_finalize_kernel, dim3(a.batch), dim3(kWave), 0, s, a.ws, a.n_slices,
+                     a.draft_ids, a.q_len, a.accept_len, a.bonus_ids, a.argmax_ids, a.kv_lens_in,
+                     a.kv_lens_out);
+}
+
+}  // namespace sv

@@ -1,0 +1,25 @@
+// Launch descriptor of the greedy-accept kernels (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+struct AcceptLaunch {
+  const float* logits;
+  const int32_t* draft_ids;
+  int32_t batch, q_len, vocab, slice, n_slices;
+  int32_t* accept_len;
+  int32_t* bonus_ids;
+  int32_t* argmax_ids;
+  const int32_t* kv_lens_in;
+  int32_t* kv_lens_out;
+  float2* ws;  // [batch*q_len, n_slices] (value, index bits)
+};
+
+constexpr int kAcceptSlice = 8192;  // vocabulary columns per argmax workgroup
+
+void launch_greedy_accept(const AcceptLaunch& a, hipStream_t s);
+
+}  // namespace sv

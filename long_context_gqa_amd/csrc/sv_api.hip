@@ -1,0 +1,323 @@
+// Host side of the C ABI declared in include/sv.h: argument validation, the
+// split planner, workspace layout and kernel launches. No allocation, no
+// host synchronisation, no device reads: every call is safe to record in a
+// HIP graph.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+
+#include "sv.h"
+#include "sv_accept.h"
+#include "sv_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sv_status fail(sv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sv_status ok() {
+  g_err[0] = 0;
+  return SV_OK;
+}
+
+sv_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Compute units of the current device, cached per device.
+int cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Plan {
+  int rb, nrg;         // row blocks of 16 per wave, row groups per workgroup
+  int splits, chunk;   // key chunks and their length in tokens
+  size_t part_o_bytes, part_lse_bytes, ws_bytes;
+};
+
+constexpr int kMinChunk = 1024;        // tokens; below this the partial traffic dominates
+constexpr int kGroupsPerCU = 2;        // workgroups per CU the automatic plan aims at
+
+sv_status validate(const sv_verify_params* p) {
+  if (!p) return fail(SV_ERR_INVALID_ARGUMENT, "params is NULL");
+  if (p->batch < 1) return fail(SV_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", p->batch);
+  if (p->q_len < 1 || p->q_len > 16)
+    return fail(SV_ERR_UNSUPPORTED, "q_len must be in 1..16 (got %d)", p->q_len);
+  if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
+    return fail(SV_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (p->q_len * G > sv::kMaxRows)
+    return fail(SV_ERR_UNSUPPORTED, "q_len * (num_q_heads/num_kv_heads) = %d exceeds %d rows per KV head",
+                p->q_len * G, sv::kMaxRows);
+  if (p->head_dim != sv::kHeadDim)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be %d (got %d)", sv::kHeadDim, p->head_dim);
+  if (p->page_size < 16 || p->page_size % 16 != 0 || p->page_size > 4096)
+    return fail(SV_ERR_UNSUPPORTED, "page_size must be a multiple of 16 in 16..4096 (got %d)", p->page_size);
+  if (p->num_pages < 1) return fail(SV_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  if (p->max_pages_per_req < 1) return fail(SV_ERR_INVALID_ARGUMENT, "max_pages_per_req must be >= 1");
+  if (p->max_kv_len < p->q_len)
+    return fail(SV_ERR_INVALID_ARGUMENT, "max_kv_len (%d) must be >= q_len (%d)", p->max_kv_len, p->q_len);
+  if ((long long)p->max_kv_len > (long long)p->max_pages_per_req * p->page_size)
+    return fail(SV_ERR_INVALID_ARGUMENT, "max_kv_len (%d) exceeds max_pages_per_req * page_size (%lld)",
+                p->max_kv_len, (long long)p->max_pages_per_req * p->page_size);
+  if (p->kv_dtype != SV_KV_FP16 && p->kv_dtype != SV_KV_FP8_E4M3)
+    return fail(SV_ERR_UNSUPPORTED, "unknown kv_dtype %d", (int)p->kv_dtype);
+  if (!(p->sm_scale > 0.f) || p->sm_scale > 1e6f)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sm_scale must be positive and finite");
+  if (p->num_splits < 0) return fail(SV_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (p->batch > 65535 || p->num_kv_heads > 65535)
+    return fail(SV_ERR_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
+  return ok();
+}
+
+sv_status make_plan(const sv_verify_params* p, Plan* pl) {
+  sv_status st = validate(p);
+  if (st != SV_OK) return st;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int R = p->q_len * G;
+  const int rbt = (R + 15) / 16;
+  if (rbt <= 3) {
+    pl->nrg = 1;
+    pl->rb = rbt;
+  } else {
+    pl->nrg = 2;
+    pl->rb = 3;
+  }
+  const long long maxkv = p->max_kv_len;
+  long long S;
+  if (p->num_splits > 0) {
+    S = p->num_splits;
+  } else {
+    const long long groups = (long long)p->batch * p->num_kv_heads;
+    const long long target = (long long)kGroupsPerCU * cu_count();
+    S = (target + groups - 1) / groups;
+    const long long cap = (maxkv + kMinChunk - 1) / kMinChunk;
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+  }
+  long long chunk = (maxkv + S - 1) / S;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  S = (maxkv + chunk - 1) / chunk;
+  pl->splits = (int)S;
+  pl->chunk = (int)chunk;
+  if (S > 1) {
+    const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
+    pl->part_o_bytes = align256((size_t)S * rows * sv::kHeadDim * sizeof(float));
+    pl->part_lse_bytes = align256((size_t)S * rows * sizeof(float));
+  } else {
+    pl->part_o_bytes = pl->part_lse_bytes = 0;
+  }
+  pl->ws_bytes = pl->part_o_bytes + pl->part_lse_bytes;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_verify_workspace_bytes(const sv_verify_params* p) {
+  Plan pl;
+  if (make_plan(p, &pl) != SV_OK) return 0;
+  return pl.ws_bytes;
+}
+
+sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t* chunk_tokens) {
+  Plan pl;
+  sv_status st = make_plan(p, &pl);
+  if (st != SV_OK) return st;
+  if (num_splits) *num_splits = pl.splits;
+  if (chunk_tokens) *chunk_tokens = pl.chunk;
+  return ok();
+}
+
+sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const void* k_pages,
+                              const void* v_pages, const void* k_scales, const void* v_scales,
+                              const int32_t* page_table, const int32_t* kv_lens, void* out,
+                              float* out_lse, void* workspace, size_t workspace_bytes,
+                              int32_t* status_flags, void* stream) {
+  Plan pl;
+  sv_status st = make_plan(p, &pl);
+  if (st != SV_OK) return st;
+  if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !out)
+    return fail(SV_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages, page_table, kv_lens and out must be non-NULL");
+  if (p->kv_dtype == SV_KV_FP8_E4M3) {
+    if (!k_scales || !v_scales)
+      return fail(SV_ERR_INVALID_ARGUMENT, "FP8 KV needs k_scales and v_scales");
+    return fail(SV_ERR_UNSUPPORTED, "FP8 E4M3 KV is not built yet");
+  } else if (k_scales || v_scales) {
+    return fail(SV_ERR_INVALID_ARGUMENT, "k_scales/v_scales must be NULL for fp16 KV");
+  }
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes)
+      return fail(SV_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", pl.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(SV_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  sv::AttnArgs a;
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.k_scales = static_cast<const _Float16*>(k_scales);
+  a.v_scales = static_cast<const _Float16*>(v_scales);
+  a.page_table = page_table;
+  a.kv_lens = kv_lens;
+  a.out = static_cast<_Float16*>(out);
+  a.out_lse = out_lse;
+  a.part_o = pl.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = pl.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes)
+                           : nullptr;
+  a.flags = status_flags;
+  a.batch = p->batch;
+  a.q_len = p->q_len;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+  a.page_size = p->page_size;
+  a.num_pages = p->num_pages;
+  a.max_pages = p->max_pages_per_req;
+  a.max_kv_len = p->max_kv_len;
+  a.chunk = pl.chunk;
+  a.num_splits = pl.splits;
+  a.scale_log2 = p->sm_scale * 1.44269504088896340736f;
+  sv::launch_verify_attention(a, pl.rb, pl.nrg, false, s);
+  st = check_launch("verify_attn");
+  if (st != SV_OK) return st;
+  if (pl.splits > 1) {
+    sv::MergeArgs m;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.out = a.out;
+    m.out_lse = out_lse;
+    m.kv_lens = kv_lens;
+    m.num_splits = pl.splits;
+    m.num_rows = p->batch * p->q_len;
+    m.num_heads = p->num_q_heads;
+    m.head_dim = sv::kHeadDim;
+    m.q_len = p->q_len;
+    m.chunk = pl.chunk;
+    m.max_kv_len = p->max_kv_len;
+    m.max_pages = p->max_pages_per_req;
+    m.page_size = p->page_size;
+    sv::launch_merge(m, s);
+    st = check_launch("verify_merge");
+    if (st != SV_OK) return st;
+  }
+  return ok();
+}
+
+sv_status sv_verify_merge(const float* part_o, const float* part_lse, int32_t num_splits,
+                          int32_t num_rows, int32_t num_heads, int32_t head_dim, void* out,
+                          float* out_lse, void* stream) {
+  if (!part_o || !part_lse || !out)
+    return fail(SV_ERR_INVALID_ARGUMENT, "part_o, part_lse and out must be non-NULL");
+  if (num_splits < 1 || num_rows < 1 || num_heads < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "num_splits, num_rows and num_heads must be >= 1");
+  if (head_dim < 4 || head_dim > 1024 || head_dim % 4 != 0)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be a multiple of 4 in 4..1024 (got %d)", head_dim);
+  if (reinterpret_cast<uintptr_t>(part_o) % 16 || reinterpret_cast<uintptr_t>(out) % 8)
+    return fail(SV_ERR_INVALID_ARGUMENT, "part_o must be 16-byte and out 8-byte aligned");
+  sv::MergeArgs m;
+  m.part_o = part_o;
+  m.part_lse = part_lse;
+  m.out = static_cast<_Float16*>(out);
+  m.out_lse = out_lse;
+  m.kv_lens = nullptr;
+  m.num_splits = num_splits;
+  m.num_rows = num_rows;
+  m.num_heads = num_heads;
+  m.head_dim = head_dim;
+  m.q_len = 1;
+  m.chunk = 1;
+  m.max_kv_len = 0;
+  m.max_pages = 0;
+  m.page_size = 0;
+  sv::launch_merge(m, static_cast<hipStream_t>(stream));
+  return check_launch("verify_merge");
+}
+
+size_t sv_greedy_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vocab) {
+  if (batch < 1 || q_len < 1 || vocab < 1) return 0;
+  const size_t slices = ((size_t)vocab + sv::kAcceptSlice - 1) / sv::kAcceptSlice;
+  return align256((size_t)batch * q_len * slices * sizeof(float2));
+}
+
+sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_t batch,
+                           int32_t q_len, int32_t vocab, int32_t* accept_len, int32_t* bonus_ids,
+                           int32_t* argmax_ids, const int32_t* kv_lens_in, int32_t* kv_lens_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 1 || q_len < 1 || vocab < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "batch, q_len and vocab must be >= 1");
+  if ((long long)batch * q_len > 65535)
+    return fail(SV_ERR_UNSUPPORTED, "batch * q_len must be <= 65535");
+  if (!logits || !accept_len || !bonus_ids)
+    return fail(SV_ERR_INVALID_ARGUMENT, "logits, accept_len and bonus_ids must be non-NULL");
+  if (q_len > 1 && !draft_ids) return fail(SV_ERR_INVALID_ARGUMENT, "draft_ids is NULL");
+  if ((kv_lens_in == nullptr) != (kv_lens_out == nullptr))
+    return fail(SV_ERR_INVALID_ARGUMENT, "kv_lens_in and kv_lens_out must be both NULL or both set");
+  if (vocab % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16)
+    return fail(SV_ERR_INVALID_ARGUMENT, "logits must be 16-byte aligned");
+  const size_t need = sv_greedy_accept_workspace_bytes(batch, q_len, vocab);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  sv::AcceptLaunch a;
+  a.logits = logits;
+  a.draft_ids = draft_ids;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.vocab = vocab;
+  a.slice = sv::kAcceptSlice;
+  a.n_slices = (vocab + sv::kAcceptSlice - 1) / sv::kAcceptSlice;
+  a.accept_len = accept_len;
+  a.bonus_ids = bonus_ids;
+  a.argmax_ids = argmax_ids;
+  a.kv_lens_in = kv_lens_in;
+  a.kv_lens_out = kv_lens_out;
+  a.ws = static_cast<float2*>(workspace);
+  sv::launch_greedy_accept(a, static_cast<hipStream_t>(stream));
+  return check_launch("greedy_accept");
+}
+
+const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_INVALID_ARGUMENT: return "SV_ERR_INVALID_ARGUMENT";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED";
+    case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL";
+    case SV_ERR_HIP: return "SV_ERR_HIP";
+  }
+  return "SV_ERR_UNKNOWN";
+}
+
+const char* sv_last_error(void) { return g_err; }
+
+int32_t sv_version(void) { return 100; }
+
+}  // extern "C"

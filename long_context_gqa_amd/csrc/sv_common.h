@@ -1,0 +1,66 @@
+// Shared device/host definitions of the HIP path (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 256;
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWave * kWavesPerGroup;
+constexpr int kStep = 16;        // tokens per wave step (one MFMA M/K block)
+constexpr int kMaxRows = 96;     // q_len * (Hq/Hkv) per KV head
+constexpr int kRowStride = kHeadDim + 4;  // fp32 LDS row stride of the combine buffer
+
+// Arguments of the verify-attention kernel (passed by value).
+struct AttnArgs {
+  const _Float16* q;
+  const void* k_pages;
+  const void* v_pages;
+  const _Float16* k_scales;
+  const _Float16* v_scales;
+  const int32_t* page_table;
+  const int32_t* kv_lens;
+  _Float16* out;
+  float* out_lse;
+  float* part_o;    // [S, B*q_len, Hq, D]
+  float* part_lse;  // [S, B*q_len, Hq]
+  int32_t* flags;
+  int32_t batch, q_len, num_q_heads, num_kv_heads, group, page_size;
+  int32_t num_pages, max_pages, max_kv_len, chunk, num_splits;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  _Float16* out;
+  float* out_lse;
+  const int32_t* kv_lens;  // optional: per-request number of chunks
+  int32_t num_splits, num_rows, num_heads, head_dim;
+  int32_t q_len, chunk, max_kv_len, max_pages, page_size;
+};
+
+// Length of request b as the kernels use it: the stored value clamped to the
+// host bound and to what the page table can address. Shared by the attention
+// and merge kernels so both see the same number of chunks.
+__device__ inline int clamp_kv_len(int raw, int max_kv_len, int max_pages, int page_size, int* flag_bits) {
+  int bound = max_kv_len;
+  long long addressable = (long long)max_pages * page_size;
+  if (addressable < bound) bound = (int)addressable;
+  int v = raw;
+  if (v > bound) { v = bound; *flag_bits |= 0x1; }
+  if (v < 0) v = 0;
+  return v;
+}
+
+void launch_verify_attention(const AttnArgs& a, int rb, int nrg, bool fp8, hipStream_t s);
+void launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace sv

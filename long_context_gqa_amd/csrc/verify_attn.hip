@@ -1,0 +1,390 @@
+// Paged causal GQA of a speculative verify block on gfx950 (fp16 KV).
+//
+// One workgroup owns one (key chunk, KV head, request). All q_len x G rows of
+// the KV head's query group ("packed rows": the verify positions folded with
+// the G query heads that share the KV head) are processed together, so every
+// K/V byte read from HBM is used by every row of the group in registers.
+//
+// Matrix-core mapping (wave64, v_mfma 16x16):
+//   S^T = K . Q^T   with 16x16x32 f16: M = 16 tokens, N = 16 rows, K = 32 channels.
+//                    A = K rows loaded straight from the page (lane = token),
+//                    B = Q fragments kept in LDS for the whole chunk.
+//   O^T = V^T . P^T with 16x16x16 f16: M = 16 channels, N = 16 rows, K = 16 tokens.
+//                    B = P^T is the S^T accumulator converted in place: the
+//                    lane that holds a row's scores also holds its softmax
+//                    state and its O accumulators, so the online-softmax
+//                    rescale needs no cross-lane traffic.
+//                    A = V^T is built from 16-byte row loads of V with a 2x2
+//                    half-word transpose (channel d of block j is
+//                    128*(j/8) + 8*lane16 + j%8).
+// The reduction order inside one MFMA is the hardware's; only the pairing of
+// A and B slots is relied on, plus the accumulator layout
+// (lane l holds rows 4*(l/16)+i, column l%16).
+//
+// The chunk's 16-token steps are dealt round-robin to the waves of the
+// workgroup (4 waves; 2 when the rows need two row groups). Each wave keeps
+// one step of K/V in flight while it computes the previous one. At the end
+// the waves' (m, l, O) are combined through LDS and the workgroup writes
+// either the final fp16 rows (request fits one chunk) or an fp32 partial
+// (o normalised, lse) for the merge kernel.
+#include "sv_common.h"
+
+namespace sv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma_16x16x16(uint32_t a0, uint32_t a1, const half4_t& b,
+                                                 floatx4 c) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 av = {a0, a1};
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// K and V of one 16-token step held by a wave: 8 x 16 B of each per lane.
+struct KFrag {
+  u32x4 k[8];  // k[s]: token lane%16, channels 32s + 8*(lane/16) .. +8
+};
+struct VFrag {
+  u32x4 v[8];  // v[2e+h]: token 4*(lane/16)+e, channels 128h + 8*(lane%16) .. +8
+};
+
+__device__ __forceinline__ void load_k(KFrag& f, const _Float16* kb, int lane) {
+  const u32x4* kp = reinterpret_cast<const u32x4*>(kb + (lane & 15) * kHeadDim + 8 * (lane >> 4));
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f.k[s] = kp[s * 4];
+}
+
+__device__ __forceinline__ void load_v(VFrag& f, const _Float16* vb, int lane) {
+  const _Float16* vr = vb + (4 * (lane >> 4)) * kHeadDim + 8 * (lane & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      f.v[2 * e + h] = *reinterpret_cast<const u32x4*>(vr + e * kHeadDim + 128 * h);
+  }
+}
+
+template <int RB>
+struct WaveState {
+  floatx4 o[RB][16];  // O^T accumulators: block j, rows of this lane
+  float m[RB];        // running max (log2 units) of row lane%16
+  float l[RB];        // this lane's share of the running sum
+};
+
+// Scores of one step, online-softmax update, and the fp16 P^T fragments.
+template <int RB>
+__device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __restrict__ qf,
+                                            WaveState<RB>& ws, half4_t (&pb)[RB], int lane, int t0,
+                                            int L, int kv, int rowbase, int R, int G,
+                                            float scale_log2) {
+  const int lo = lane & 15, hi = lane >> 4;
+  const bool tail = (t0 + kStep > L + 1);  // some key here is hidden from some row
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Q is re-read from LDS every step; the opaque offset keeps the compiler
+    // from hoisting 32*RB registers of fragments out of the loop.
+    int qo = rb * 8 * kWave + lane;
+    asm volatile("" : "+v"(qo));
+    u32x4 qv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = mfma_16x16x32(kf.k[s], qv[s], acc);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = acc[i] * scale_log2;
+    if (tail) {
+      const int r = rowbase + rb * 16 + lo;
+      int lim = kv;
+      if (r < R) lim = min(L + r / G + 1, kv);
+      const int tok = t0 + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tok + i >= lim) x[i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(ws.m[rb], mx);
+    const float ref = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = exp2_fast(ws.m[rb] - ref);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[i] - ref);
+    ws.l[rb] = ws.l[rb] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    ws.m[rb] = mnew;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ws.o[rb][j] *= alpha;
+    }
+    pb[rb] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+  }
+}
+
+// O^T += V^T . P^T for one step.
+template <int RB>
+__device__ __forceinline__ void step_pv(VFrag& vf, const half4_t (&pb)[RB], WaveState<RB>& ws,
+                                        int lane, int t0, int kv) {
+  const int hi = lane >> 4;
+  // Keys at or past kv_len may be poison in the page's unused slots; their
+  // weight is exactly 0 but 0 * NaN is NaN, so clear those V rows.
+  if (t0 + kStep > kv) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (t0 + 4 * hi + e >= kv) {
+        vf.v[2 * e] = u32x4{0u, 0u, 0u, 0u};
+        vf.v[2 * e + 1] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      const uint32_t w0 = vf.v[h][c2], w1 = vf.v[2 + h][c2];
+      const uint32_t w2 = vf.v[4 + h][c2], w3 = vf.v[6 + h][c2];
+      const uint32_t lo0 = (w0 & 0xffffu) | (w1 << 16), lo1 = (w2 & 0xffffu) | (w3 << 16);
+      const uint32_t hi0 = (w0 >> 16) | (w1 & 0xffff0000u), hi1 = (w2 >> 16) | (w3 & 0xffff0000u);
+      const int j = 8 * h + 2 * c2;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        ws.o[rb][j] = mfma_16x16x16(lo0, lo1, pb[rb], ws.o[rb][j]);
+        ws.o[rb][j + 1] = mfma_16x16x16(hi0, hi1, pb[rb], ws.o[rb][j + 1]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <int RB, int NRG>
+__global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a) {
+  constexpr int NTS = kWavesPerGroup / NRG;   // waves sharing one row group
+  constexpr int QBYTES = NRG * RB * 8 * kWave * 16;
+  constexpr int OBYTES = NRG * RB * 16 * kRowStride * 4;
+  constexpr int UBYTES = QBYTES > OBYTES ? QBYTES : OBYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[UBYTES];
+  __shared__ float s_m[NTS][NRG * RB * 16];
+  __shared__ float s_l[NTS][NRG * RB * 16];
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int rg = wave % NRG, ts = wave / NRG;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int q_len = a.q_len, G = a.group, R = q_len * G, Hq = a.num_q_heads;
+
+  int flag_bits = 0;
+  const int raw_kv = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
+  const int kv = clamp_kv_len(raw_kv, a.max_kv_len, a.max_pages, a.page_size, &flag_bits);
+  if (raw_kv < q_len) flag_bits |= 0x2;
+  const int n_chunks = kv > 0 ? (kv + a.chunk - 1) / a.chunk : 1;
+  const int chunk_lo = split * a.chunk;
+  if (split >= n_chunks) return;  // whole group: nothing of this request here
+  const int chunk_hi = min(chunk_lo + a.chunk, kv);
+  const int L = kv - q_len;
+  const bool direct = (n_chunks == 1);
+  if (tid == 0) s_flag = 0;
+
+  // Q fragments of every row group into LDS, in MFMA B-operand order.
+  u32x4* qlds = reinterpret_cast<u32x4*>(smem);
+  for (int idx = tid; idx < NRG * RB * 8 * kWave; idx += kThreads) {
+    const int frag = idx / kWave, ln = idx % kWave;
+    const int rgi = frag / (RB * 8), rb = (frag / 8) % RB, s = frag % 8;
+    const int r = (rgi * RB + rb) * 16 + (ln & 15);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R) {
+      const int i = r / G, j = r % G;
+      const _Float16* src =
+          a.q + ((size_t)(b * q_len + i) * Hq + g * G + j) * kHeadDim + 32 * s + 8 * (ln >> 4);
+      v = *reinterpret_cast<const u32x4*>(src);
+    }
+    qlds[idx] = v;
+  }
+  __syncthreads();
+
+  WaveState<RB> ws;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    ws.m[rb] = -INFINITY;
+    ws.l[rb] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ws.o[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const u32x4* qf = qlds + rg * RB * 8 * kWave;
+  const int rowbase = rg * RB * 16;
+  const int n_steps = (chunk_hi > chunk_lo) ? (chunk_hi - chunk_lo + kStep - 1) / kStep : 0;
+  const int my_steps = n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0;
+  const int P = a.page_size, Hkv = a.num_kv_heads;
+  const _Float16* kpool = static_cast<const _Float16*>(a.k_pages);
+  const _Float16* vpool = static_cast<const _Float16*>(a.v_pages);
+  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+
+  for (int bstart = 0; bstart < my_steps; bstart += kWave) {
+    // page id of each of the next 64 steps of this wave, one per lane
+    int pid = 0;
+    {
+      const int kl = bstart + lane;
+      if (kl < my_steps) {
+        const int t = chunk_lo + kStep * (ts + kl * NTS);
+        pid = ptab[t / P];
+        if (pid < 0 || pid >= a.num_pages) {
+          flag_bits |= 0x4;
+          pid = 0;
+        }
+      }
+    }
+    const int nb = min(kWave, my_steps - bstart);
+    auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
+    auto step_base = [&](int kk, const _Float16* pool) {
+      const int t0 = step_t0(kk);
+      const int pg = __builtin_amdgcn_readlane(pid, kk);
+      return pool + (((size_t)pg * Hkv + g) * P + (t0 % P)) * kHeadDim;
+    };
+    // One K and one V register buffer. The next step's K is requested as soon
+    // as the scores have consumed the current K, the next V as soon as the PV
+    // product has consumed the current V, so about one step per wave is in
+    // flight at any time. Loads are unconditional (the index is clamped; the
+    // duplicate request of the last step hits in cache) so the compiler waits
+    // for exactly the older buffer instead of draining every load.
+    KFrag kf;
+    VFrag vf;
+    load_k(kf, step_base(0, kpool), lane);
+    load_v(vf, step_base(0, vpool), lane);
+    for (int kk = 0; kk < nb; ++kk) {
+      const int t0 = step_t0(kk);
+      const int kn = min(kk + 1, nb - 1);
+      half4_t pb[RB];
+      step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, rowbase, R, G, a.scale_log2);
+      load_k(kf, step_base(kn, kpool), lane);
+      step_pv<RB>(vf, pb, ws, lane, t0, kv);
+      load_v(vf, step_base(kn, vpool), lane);
+    }
+  }
+
+  // ---- combine the waves of each row group --------------------------------
+  const int lo = lane & 15, hi = lane >> 4;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float lr = ws.l[rb];
+    lr += __shfl_xor(lr, 16);
+    lr += __shfl_xor(lr, 32);
+    if (hi == 0) {
+      s_m[ts][rowbase + rb * 16 + lo] = ws.m[rb];
+      s_l[ts][rowbase + rb * 16 + lo] = lr;
+    }
+  }
+  if (flag_bits) atomicOr(&s_flag, flag_bits);
+  __syncthreads();  // every wave is past its main loop: Q area may be reused
+
+  float lse_row[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = rowbase + rb * 16 + lo;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NTS; ++k) M = fmaxf(M, s_m[k][row]);
+    const float Mref = (M == -INFINITY) ? 0.f : M;
+    float Ls = 0.f;
+#pragma unroll
+    for (int k = 0; k < NTS; ++k) Ls += s_l[k][row] * exp2_fast(s_m[k][row] - Mref);
+    const float f = Ls > 0.f ? exp2_fast(ws.m[rb] - Mref) / Ls : 0.f;
+    lse_row[rb] = Ls > 0.f ? (Mref + log2f(Ls)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ws.o[rb][j] *= f;
+  }
+
+  float* obuf = reinterpret_cast<float*>(smem);
+  for (int k = 0; k < NTS; ++k) {
+    if (ts == k) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float* rowp = obuf + (rowbase + rb * 16 + lo) * kRowStride;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float4* dst = reinterpret_cast<float4*>(rowp + 128 * h + 32 * hi + 8 * i);
+            float4 v0 = make_float4(ws.o[rb][8 * h + 0][i], ws.o[rb][8 * h + 1][i],
+                                    ws.o[rb][8 * h + 2][i], ws.o[rb][8 * h + 3][i]);
+            float4 v1 = make_float4(ws.o[rb][8 * h + 4][i], ws.o[rb][8 * h + 5][i],
+                                    ws.o[rb][8 * h + 6][i], ws.o[rb][8 * h + 7][i]);
+            if (k == 0) {
+              dst[0] = v0;
+              dst[1] = v1;
+            } else {
+              float4 a0 = dst[0], a1 = dst[1];
+              dst[0] = make_float4(a0.x + v0.x, a0.y + v0.y, a0.z + v0.z, a0.w + v0.w);
+              dst[1] = make_float4(a1.x + v1.x, a1.y + v1.y, a1.z + v1.z, a1.w + v1.w);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // lse of each row (one writer per row)
+  if (ts == 0 && hi == 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = rowbase + rb * 16 + lo;
+      if (r < R) {
+        const int i = r / G, j = r % G;
+        const size_t orow = (size_t)(b * q_len + i) * Hq + g * G + j;
+        if (direct) {
+          if (a.out_lse) a.out_lse[orow] = lse_row[rb];
+        } else {
+          a.part_lse[(size_t)split * a.batch * q_len * Hq + orow] = lse_row[rb];
+        }
+      }
+    }
+  }
+  // rows out: 32 threads per row, 8 channels per thread
+  for (int r = tid / 32; r < R; r += kThreads / 32) {
+    const int d0 = (tid % 32) * 8;
+    const float* src = obuf + r * kRowStride + d0;
+    const float4 v0 = *reinterpret_cast<const float4*>(src);
+    const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+    const int i = r / G, j = r % G;
+    const size_t orow = (size_t)(b * q_len + i) * Hq + g * G + j;
+    if (direct) {
+      half8_t hv = {(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
+                    (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
+      *reinterpret_cast<half8_t*>(a.out + orow * kHeadDim + d0) = hv;
+    } else {
+      float* dst = a.part_o + ((size_t)split * a.batch * q_len * Hq + orow) * kHeadDim + d0;
+      reinterpret_cast<float4*>(dst)[0] = v0;
+      reinterpret_cast<float4*>(dst)[1] = v1;
+    }
+  }
+  if (tid == 0 && s_flag && a.flags) atomicOr(a.flags, s_flag);
+}
+
+void launch_verify_attention(const AttnArgs& a, int rb, int nrg, bool fp8, hipStream_t s) {
+  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  dim3 block(kThreads);
+  (void)fp8;
+  if (nrg == 1) {
+    if (rb == 1) hipLaunchKernelGGL((verify_attn_f16_kernel<1, 1>), grid, block, 0, s, a);
+    else if (rb == 2) hipLaunchKernelGGL((verify_attn_f16_kernel<2, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_attn_f16_kernel<3, 1>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((verify_attn_f16_kernel<3, 2>), grid, block, 0, s, a);
+  }
+}
+
+}  // namespace sv

@@ -1,0 +1,112 @@
+"""The C ABI library loads, exports every entry point include/sv.h declares,
+and rejects bad arguments on the host without launching (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_gqa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "sv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for n in ("sv_verify_attention", "sv_verify_merge", "sv_greedy_accept"):
+        assert n in names
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    for n in declared_symbols():
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    lib = B.lib()
+    assert lib.sv_status_string(0) == b"SV_OK"
+    assert lib.sv_status_string(3) == b"SV_ERR_WORKSPACE_TOO_SMALL"
+    assert B.sv_version() >= 100
+
+
+def _p(**kw):
+    base = dict(batch=1, q_len=8, num_q_heads=24, num_kv_heads=4, head_dim=256, page_size=16,
+                num_pages=300, max_pages_per_req=257, max_kv_len=4104)
+    base.update(kw)
+    return B.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_len=0), B.SV_ERR_UNSUPPORTED),
+    (dict(q_len=17), B.SV_ERR_UNSUPPORTED),
+    (dict(head_dim=128), B.SV_ERR_UNSUPPORTED),
+    (dict(num_q_heads=25), B.SV_ERR_INVALID_ARGUMENT),
+    (dict(page_size=24), B.SV_ERR_UNSUPPORTED),
+    (dict(max_kv_len=7), B.SV_ERR_INVALID_ARGUMENT),
+    (dict(max_kv_len=5000), B.SV_ERR_INVALID_ARGUMENT),  # beyond max_pages_per_req * page_size
+    (dict(num_q_heads=48, num_kv_heads=2, q_len=8), B.SV_ERR_UNSUPPORTED),  # 192 rows per KV head
+    (dict(batch=0), B.SV_ERR_INVALID_ARGUMENT),
+])
+def test_plan_rejects_bad_shapes(kw, status):
+    with pytest.raises(B.SvError) as e:
+        B.sv_verify_plan(_p(**kw))
+    assert e.value.status == status
+    assert B.sv_verify_workspace_bytes(_p(**kw)) == 0
+
+
+def test_plan_chunks_are_anchored_multiples_of_64():
+    for maxkv in (8, 100, 4104, 32776, 524296):
+        p = _p(max_kv_len=maxkv, max_pages_per_req=(maxkv + 15) // 16, num_pages=(maxkv + 15) // 16)
+        s, c = B.sv_verify_plan(p)
+        assert c % 64 == 0 and s == -(-maxkv // c)
+        assert (B.sv_verify_workspace_bytes(p) == 0) == (s == 1)
+    for forced in (1, 2, 3, 7, 64):
+        p = _p(num_splits=forced)
+        s, c = B.sv_verify_plan(p)
+        assert s <= forced and s == -(-4104 // c)
+
+
+def test_null_pointers_rejected_without_launch():
+    lib = B.lib()
+    p = _p()
+    st = lib.sv_verify_attention(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
+                                 None, 0, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT
+    assert b"non-NULL" in lib.sv_last_error()
+    st = lib.sv_verify_merge(None, None, 1, 1, 1, 256, None, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT
+    st = lib.sv_greedy_accept(None, None, 1, 8, 100, None, None, None, None, None, None, 0, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_too_small_rejected_without_launch():
+    lib = B.lib()
+    p = _p(num_splits=4)
+    fake = 1 << 40  # never dereferenced: the call must fail before any launch
+    st = lib.sv_verify_attention(ctypes.byref(p), fake, fake, fake, None, None, fake, fake, fake, None,
+                                 fake, 16, None, None)
+    assert st == B.SV_ERR_WORKSPACE_TOO_SMALL
+    need = lib.sv_greedy_accept_workspace_bytes(2, 8, 248320)
+    assert need == ((2 * 8 * 31 * 8 + 255) // 256) * 256
+    st = lib.sv_greedy_accept(fake, fake, 2, 8, 248320, fake, fake, None, None, None, fake, need - 1, None)
+    assert st == B.SV_ERR_WORKSPACE_TOO_SMALL
+    st = lib.sv_greedy_accept(fake, fake, 2, 8, 248320, fake, fake, None, fake, None, fake, need, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT  # kv_lens_in without kv_lens_out
+
+
+def test_fp16_with_scales_rejected():
+    lib = B.lib()
+    p = _p()
+    fake = 1 << 40
+    st = lib.sv_verify_attention(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None,
+                                 fake, 1 << 30, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT
