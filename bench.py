@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--variant", default="literal", choices=["literal", "unit"])
     ap.add_argument("--splits", type=int, default=0, help="force the number of key chunks (0 = planner)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-splits", default=None,
+                    help="comma-separated split counts: time the verify attention call at each")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per verify_attn launch (FETCH+WRITE)")
     return ap.parse_args()
@@ -64,6 +68,17 @@ def main():
     B.lib()  # fail loudly if libsv.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+        # the scale between counter units and bytes moved
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
     wl = W.WORKLOADS[args.config]
     log(f"[bench] workload {wl.name} ({args.variant}): generating inputs on the GPU")
     t0 = time.time()
@@ -145,6 +160,21 @@ def main():
         with open(args.traffic) as f:
             traffic = json.load(f).get("bytes_per_launch")
 
+    sweep = None
+    if args.sweep_splits:
+        sweep = {}
+        for sp in [int(v) for v in args.sweep_splits.split(",")]:
+            c2 = B.VerifyCall(x.q, x.k_pages, x.v_pages, page_table, kv_lens, wl.q_len, x.max_kv_len,
+                              x.k_scales, x.v_scales, x.sm_scale, sp)
+            for _ in range(3):
+                c2.run(stream)
+            us = float(np.median(timed(lambda: c2.run(stream), n_part)))
+            sweep[str(c2.splits)] = {"us": round(us, 2), "chunk": c2.chunk,
+                                     "GBps": round(attn_bytes / (us * 1e-6) / 1e9, 1)}
+            log(f"[bench] splits {c2.splits:4d} chunk {c2.chunk:6d}: {us:8.2f} us  "
+                f"{attn_bytes / (us * 1e-6) / 1e9:8.1f} GB/s")
+            del c2
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wl)
@@ -197,6 +227,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
+        "split_sweep": sweep,
     }
     print(json.dumps(res), flush=True)
 

@@ -2,9 +2,10 @@
 // final fp16 rows: LSE = ln sum_s exp(lse_s), out = sum_s exp(lse_s - LSE) o_s,
 // skipping empty splits (lse = -inf).
 //
-// One wave per (row, head): the lanes first reduce the split lse values
-// (max, then sum of exponentials), then each lane accumulates a float4 slice
-// of the channels over the splits — reads of one split are 1 KB contiguous.
+// One workgroup per (row, head). Its threads first reduce the split lse
+// values (max, then the sum of exponentials); then wave w accumulates splits
+// w, w+4, ... with each lane owning a float4 of channels and four splits'
+// loads in flight at a time; the four waves' sums are added through LDS.
 #include "sv_common.h"
 
 namespace sv {
@@ -25,11 +26,22 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 }  // namespace
 
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int k = 1; k < kWavesPerGroup; ++k) r = is_max ? fmaxf(r, red[k]) : r + red[k];
+  return r;
+}
+
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  const int lane = threadIdx.x % kWave;
-  const long long item = (long long)blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
-  const long long n_items = (long long)a.num_rows * a.num_heads;
-  if (item >= n_items) return;
+  __shared__ float red[kWavesPerGroup];
+  __shared__ float4 acc_s[kWavesPerGroup - 1][kWave];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const long long item = blockIdx.x;  // (row, head)
   const int row = (int)(item / a.num_heads);
   int S = a.num_splits;
   if (a.kv_lens) {
@@ -42,48 +54,83 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     if (nch <= 1) return;
     S = min(S, nch);
   }
-  const size_t split_stride_l = (size_t)a.num_rows * a.num_heads;
-  const size_t split_stride_o = split_stride_l * a.head_dim;
+  const size_t sl = (size_t)a.num_rows * a.num_heads;  // stride between splits (lse)
+  const size_t so = sl * a.head_dim;                     // stride between splits (o)
+  const float* lse = a.part_lse + item;
+  const float* po = a.part_o + item * a.head_dim;
 
   float mx = -INFINITY;
-  for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, a.part_lse[(size_t)s * split_stride_l + item]);
-  mx = wave_max(mx);
+  for (int s = threadIdx.x; s < S; s += kThreads) mx = fmaxf(mx, lse[s * sl]);
+  mx = block_reduce(mx, red, true);
   const float ref = (mx == -INFINITY) ? 0.f : mx;
   float tot = 0.f;
-  for (int s = lane; s < S; s += kWave) {
-    const float l = a.part_lse[(size_t)s * split_stride_l + item];
+  for (int s = threadIdx.x; s < S; s += kThreads) {
+    const float l = lse[s * sl];
     tot += (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((l - ref) * kLog2e);
   }
-  tot = wave_sum(tot);
+  tot = block_reduce(tot, red, false);
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 
   const int D4 = a.head_dim / 4;
-  for (int d4 = lane; d4 < D4; d4 += kWave) {
+  // uniform trip count: every lane passes the same barriers
+  for (int base = 0; base < D4; base += kWave) {
+    const int d4 = base + lane;
+    const bool on = d4 < D4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < S; ++s) {
-      const float l = a.part_lse[(size_t)s * split_stride_l + item];
-      if (l == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f((l - ref) * kLog2e);
-      const float4 o = reinterpret_cast<const float4*>(a.part_o + (size_t)s * split_stride_o +
-                                                       item * a.head_dim)[d4];
-      acc.x += w * o.x;
-      acc.y += w * o.y;
-      acc.z += w * o.z;
-      acc.w += w * o.w;
+    if (on) {
+      int s = w;
+      for (; s + 3 * kWavesPerGroup < S; s += 4 * kWavesPerGroup) {
+        float l[4];
+        float4 o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          l[u] = lse[(s + u * kWavesPerGroup) * sl];
+          o[u] = reinterpret_cast<const float4*>(po + (s + u * kWavesPerGroup) * so)[d4];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wgt = (l[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((l[u] - ref) * kLog2e);
+          acc.x += wgt * o[u].x;
+          acc.y += wgt * o[u].y;
+          acc.z += wgt * o[u].z;
+          acc.w += wgt * o[u].w;
+        }
+      }
+      for (; s < S; s += kWavesPerGroup) {
+        const float l = lse[s * sl];
+        const float wgt = (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((l - ref) * kLog2e);
+        const float4 o = reinterpret_cast<const float4*>(po + s * so)[d4];
+        acc.x += wgt * o.x;
+        acc.y += wgt * o.y;
+        acc.z += wgt * o.z;
+        acc.w += wgt * o.w;
+      }
+      if (w > 0) acc_s[w - 1][lane] = acc;
     }
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    h4 hv = {(_Float16)(acc.x * inv), (_Float16)(acc.y * inv), (_Float16)(acc.z * inv),
-             (_Float16)(acc.w * inv)};
-    reinterpret_cast<h4*>(a.out + item * a.head_dim)[d4] = hv;
+    __syncthreads();
+    if (w == 0 && on) {
+#pragma unroll
+      for (int k = 0; k < kWavesPerGroup - 1; ++k) {
+        const float4 t = acc_s[k][lane];
+        acc.x += t.x;
+        acc.y += t.y;
+        acc.z += t.z;
+        acc.w += t.w;
+      }
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      h4 hv = {(_Float16)(acc.x * inv), (_Float16)(acc.y * inv), (_Float16)(acc.z * inv),
+               (_Float16)(acc.w * inv)};
+      reinterpret_cast<h4*>(a.out + item * a.head_dim)[d4] = hv;
+    }
+    __syncthreads();
   }
-  if (a.out_lse && lane == 0)
+  if (a.out_lse && threadIdx.x == 0)
     a.out_lse[item] = tot > 0.f ? ref + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
 }
 
 void launch_merge(const MergeArgs& a, hipStream_t s) {
   const long long n_items = (long long)a.num_rows * a.num_heads;
-  const unsigned blocks = (unsigned)((n_items + kWavesPerGroup - 1) / kWavesPerGroup);
-  hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace sv

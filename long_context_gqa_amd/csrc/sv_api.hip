@@ -58,8 +58,9 @@ struct Plan {
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
 
-constexpr int kMinChunk = 1024;        // tokens; below this the partial traffic dominates
-constexpr int kGroupsPerCU = 2;        // workgroups per CU the automatic plan aims at
+constexpr int kMinChunk = 128;         // tokens; below this the partial traffic dominates
+constexpr int kBatchChunkCap = 8192;   // tokens; largest automatic chunk for a batch of requests
+constexpr int kGroupsPerCU = 1;        // workgroups per CU the automatic plan aims at (LDS and registers allow one)
 
 sv_status validate(const sv_verify_params* p) {
   if (!p) return fail(SV_ERR_INVALID_ARGUMENT, "params is NULL");
@@ -108,15 +109,21 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     pl->rb = 3;
   }
   const long long maxkv = p->max_kv_len;
+  const long long rgs = 1;  // workgroups per (chunk, KV head, request)
   long long S;
   if (p->num_splits > 0) {
     S = p->num_splits;
   } else {
-    const long long groups = (long long)p->batch * p->num_kv_heads;
+    // Enough chunks for one workgroup per CU when every request is as long as
+    // max_kv_len; for batches (whose lengths may be ragged) also cap the chunk
+    // so that the work is cut into pieces small enough to balance.
+    const long long groups = (long long)p->batch * p->num_kv_heads * rgs;
     const long long target = (long long)kGroupsPerCU * cu_count();
     S = (target + groups - 1) / groups;
-    const long long cap = (maxkv + kMinChunk - 1) / kMinChunk;
-    if (S > cap) S = cap;
+    long long chunk = (maxkv + S - 1) / S;
+    if (p->batch > 1 && chunk > kBatchChunkCap) chunk = kBatchChunkCap;
+    if (chunk < kMinChunk) chunk = kMinChunk;
+    S = (maxkv + chunk - 1) / chunk;
     if (S < 1) S = 1;
   }
   long long chunk = (maxkv + S - 1) / S;
@@ -206,7 +213,7 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
   a.chunk = pl.chunk;
   a.num_splits = pl.splits;
   a.scale_log2 = p->sm_scale * 1.44269504088896340736f;
-  sv::launch_verify_attention(a, pl.rb, pl.nrg, false, s);
+  sv::launch_verify_attention(a, pl.rb, pl.nrg, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
   if (pl.splits > 1) {

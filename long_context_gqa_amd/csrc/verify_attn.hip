@@ -36,6 +36,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazyLog2 = 8.f;  // largest p = 256 between rescales
 
 __device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -59,26 +60,35 @@ struct VFrag {
   u32x4 v[8];  // v[2e+h]: token 4*(lane/16)+e, channels 128h + 8*(lane%16) .. +8
 };
 
-__device__ __forceinline__ void load_k(KFrag& f, const _Float16* kb, int lane) {
-  const u32x4* kp = reinterpret_cast<const u32x4*>(kb + (lane & 15) * kHeadDim + 8 * (lane >> 4));
-#pragma unroll
-  for (int s = 0; s < 8; ++s) f.k[s] = kp[s * 4];
-}
-
-__device__ __forceinline__ void load_v(VFrag& f, const _Float16* vb, int lane) {
-  const _Float16* vr = vb + (4 * (lane >> 4)) * kHeadDim + 8 * (lane & 15);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      f.v[2 * e + h] = *reinterpret_cast<const u32x4*>(vr + e * kHeadDim + 128 * h);
-  }
+// Multiply one accumulator tuple by a per-lane factor in place. Done in
+// inline asm on the accumulation registers themselves, so the compiler does
+// not keep shadow copies of all accumulators in ordinary registers for the
+// (rarely taken) rescale branch.
+__device__ __forceinline__ void scale_acc(floatx4& acc, float f) {
+  float e0 = acc[0], e1 = acc[1], e2 = acc[2], e3 = acc[3];
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %4, %0\n\t"
+      "v_mul_f32 %4, %5, %4\n\t"
+      "v_accvgpr_write_b32 %0, %4\n\t"
+      "v_accvgpr_read_b32 %4, %1\n\t"
+      "v_mul_f32 %4, %5, %4\n\t"
+      "v_accvgpr_write_b32 %1, %4\n\t"
+      "v_accvgpr_read_b32 %4, %2\n\t"
+      "v_mul_f32 %4, %5, %4\n\t"
+      "v_accvgpr_write_b32 %2, %4\n\t"
+      "v_accvgpr_read_b32 %4, %3\n\t"
+      "v_mul_f32 %4, %5, %4\n\t"
+      "v_accvgpr_write_b32 %3, %4"
+      : "+a"(e0), "+a"(e1), "+a"(e2), "+a"(e3), "=&v"(t)
+      : "v"(f));
+  acc = floatx4{e0, e1, e2, e3};
 }
 
 template <int RB>
 struct WaveState {
   floatx4 o[RB][16];  // O^T accumulators: block j, rows of this lane
-  float m[RB];        // running max (log2 units) of row lane%16
+  float m[RB];        // reference (log2 units, >= every score seen - 8) of row lane%16
   float l[RB];        // this lane's share of the running sum
 };
 
@@ -117,18 +127,25 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(ws.m[rb], mx);
-    const float ref = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = exp2_fast(ws.m[rb] - ref);
+    // Lazy reference: the row's reference m only moves when the tile max
+    // exceeds it by more than kLazyLog2, so p = 2^(x - m) <= 2^kLazyLog2 stays
+    // well inside fp16 and the O/l rescale (192 accumulators) is rare.
+    // Numerator and denominator share the reference, so the result is the
+    // same softmax.
+    const bool bump = mx > ws.m[rb] + kLazyLog2;
+    if (__any(bump)) {
+      const float mnew = bump ? mx : ws.m[rb];
+      const float alpha = bump ? exp2_fast(ws.m[rb] - mnew) : 1.f;  // m = -inf -> 0
+      ws.l[rb] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) scale_acc(ws.o[rb][j], alpha);
+      ws.m[rb] = mnew;
+    }
+    const float ref = (ws.m[rb] == -INFINITY) ? 0.f : ws.m[rb];
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[i] - ref);
-    ws.l[rb] = ws.l[rb] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    ws.m[rb] = mnew;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ws.o[rb][j] *= alpha;
-    }
+    ws.l[rb] += (p[0] + p[1]) + (p[2] + p[3]);
     pb[rb] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
   }
 }
@@ -169,13 +186,98 @@ __device__ __forceinline__ void step_pv(VFrag& vf, const half4_t (&pb)[RB], Wave
 
 }  // namespace
 
+// LDS addresses are 32-bit; the ring is read with inline-asm ds_read_b128 so
+// that the compiler does not drain every outstanding DMA before each read
+// (it cannot tell which DMA a read depends on); the waits are explicit.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)(p));
+}
+
+#define SV_GP(p) ((__attribute__((address_space(1))) void*)(p))
+#define SV_LP(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Eight 16-byte reads from one 8 KB ring block after waiting until at most
+// VMCNT of this wave's vector-memory operations (the newer half-steps) are
+// outstanding, i.e. until the block's own DMA has landed; with BARRIER the
+// workgroup also meets, so blocks DMA-ed by the partner wave have landed too.
+template <int VMCNT, bool BARRIER>
+__device__ __forceinline__ void ring_read8(u32x4 (&d)[8], uint32_t addr) {
+  if constexpr (BARRIER) {
+    asm volatile(
+        "s_waitcnt vmcnt(%9)\n\t"
+        "s_barrier\n\t"
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(d[0]), "=v"(d[1]), "=v"(d[2]), "=v"(d[3]), "=v"(d[4]), "=v"(d[5]), "=v"(d[6]), "=v"(d[7])
+        : "v"(addr), "n"(VMCNT)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_waitcnt vmcnt(%9)\n\t"
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(d[0]), "=v"(d[1]), "=v"(d[2]), "=v"(d[3]), "=v"(d[4]), "=v"(d[5]), "=v"(d[6]), "=v"(d[7])
+        : "v"(addr), "n"(VMCNT)
+        : "memory");
+  }
+}
+
+// Direct HBM -> LDS copies of 1 KB blocks [B0, B1) of one half-step: lane l
+// of block j lands at ring + j*1024 + 16*l (the order the MFMA operand reads
+// it). K block j = channels 32j + 8*(lane/16) of token lane%16; V block 2e+h
+// = channels 128h + 8*(lane%16) of token 4*(lane/16)+e.
+template <int B0, int B1>
+__device__ __forceinline__ void dma_k(const _Float16* kb, char* ring, int lane) {
+  const _Float16* src = kb + (lane & 15) * kHeadDim + 8 * (lane >> 4);
+#pragma unroll
+  for (int s = B0; s < B1; ++s)
+    __builtin_amdgcn_global_load_lds(SV_GP(src + 32 * s), SV_LP(ring + s * 1024), 16, 0, 0);
+}
+template <int B0, int B1>
+__device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) {
+  const _Float16* src = vb + (4 * (lane >> 4)) * kHeadDim + 8 * (lane & 15);
+#pragma unroll
+  for (int j = B0; j < B1; ++j)
+    __builtin_amdgcn_global_load_lds(SV_GP(src + (j >> 1) * kHeadDim + 128 * (j & 1)),
+                                     SV_LP(ring + j * 1024), 16, 0, 0);
+}
+
+constexpr int kRingStage = 16384;               // K (8 KB) + V (8 KB) of one step
+constexpr int kRingPerWave = 2 * kRingStage;    // two stages per wave
+
+template <int RB, int NRG>
+struct Smem {
+  static constexpr int NTS = kWavesPerGroup / NRG;
+  static constexpr int QBYTES = NRG * RB * 8 * kWave * 16;
+  static constexpr int OBYTES = NRG * RB * 16 * kRowStride * 4;
+  // NRG 1: a private 2-stage ring per wave; NRG 2: a 3-stage ring per pair
+  static constexpr int RBYTES = NRG == 1 ? kWavesPerGroup * kRingPerWave : NTS * 3 * kRingStage;
+  // Q fragments in their own array (so reading them never waits for the
+  // ring's DMAs); the ring and, after the main loop, the combine buffer
+  // share the second array.
+  static constexpr int BIG = RBYTES > OBYTES ? RBYTES : OBYTES;
+};
+
 template <int RB, int NRG>
 __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a) {
-  constexpr int NTS = kWavesPerGroup / NRG;   // waves sharing one row group
-  constexpr int QBYTES = NRG * RB * 8 * kWave * 16;
-  constexpr int OBYTES = NRG * RB * 16 * kRowStride * 4;
-  constexpr int UBYTES = QBYTES > OBYTES ? QBYTES : OBYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[UBYTES];
+  using SM = Smem<RB, NRG>;
+  constexpr int NTS = SM::NTS;   // waves sharing one row group
+  __shared__ __attribute__((aligned(1024))) unsigned char qsm[SM::QBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char bigsm[SM::BIG];
   __shared__ float s_m[NTS][NRG * RB * 16];
   __shared__ float s_l[NTS][NRG * RB * 16];
   __shared__ int s_flag;
@@ -183,7 +285,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int rg = wave % NRG, ts = wave / NRG;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x;
+  const int row0 = 0;  // first row (of the KV head's q_len*G) of this workgroup
   const int q_len = a.q_len, G = a.group, R = q_len * G, Hq = a.num_q_heads;
 
   int flag_bits = 0;
@@ -199,11 +303,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
   if (tid == 0) s_flag = 0;
 
   // Q fragments of every row group into LDS, in MFMA B-operand order.
-  u32x4* qlds = reinterpret_cast<u32x4*>(smem);
+  u32x4* qlds = reinterpret_cast<u32x4*>(qsm);
   for (int idx = tid; idx < NRG * RB * 8 * kWave; idx += kThreads) {
     const int frag = idx / kWave, ln = idx % kWave;
     const int rgi = frag / (RB * 8), rb = (frag / 8) % RB, s = frag % 8;
-    const int r = (rgi * RB + rb) * 16 + (ln & 15);
+    const int r = row0 + (rgi * RB + rb) * 16 + (ln & 15);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < R) {
       const int i = r / G, j = r % G;
@@ -225,53 +329,139 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
   }
 
   const u32x4* qf = qlds + rg * RB * 8 * kWave;
-  const int rowbase = rg * RB * 16;
+  const int rowbase = rg * RB * 16;        // first row of this wave, local to the workgroup
+  const int growbase = row0 + rowbase;     // the same row in the KV head's numbering
   const int n_steps = (chunk_hi > chunk_lo) ? (chunk_hi - chunk_lo + kStep - 1) / kStep : 0;
   const int my_steps = n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0;
   const int P = a.page_size, Hkv = a.num_kv_heads;
   const _Float16* kpool = static_cast<const _Float16*>(a.k_pages);
   const _Float16* vpool = static_cast<const _Float16*>(a.v_pages);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
-
-  for (int bstart = 0; bstart < my_steps; bstart += kWave) {
-    // page id of each of the next 64 steps of this wave, one per lane
-    int pid = 0;
-    {
-      const int kl = bstart + lane;
-      if (kl < my_steps) {
-        const int t = chunk_lo + kStep * (ts + kl * NTS);
-        pid = ptab[t / P];
-        if (pid < 0 || pid >= a.num_pages) {
-          flag_bits |= 0x4;
-          pid = 0;
+  if constexpr (NRG == 1) {
+    // ---- each wave owns its token steps and a private 2-stage LDS ring ----
+    char* ring = reinterpret_cast<char*>(bigsm) + wave * kRingPerWave;
+    for (int bstart = 0; bstart < my_steps; bstart += kWave) {
+      // page id of each of the next 64 steps of this wave, one per lane
+      int pid = 0;
+      {
+        const int kl = bstart + lane;
+        if (kl < my_steps) {
+          const int t = chunk_lo + kStep * (ts + kl * NTS);
+          pid = ptab[t / P];
+          if (pid < 0 || pid >= a.num_pages) {
+            flag_bits |= 0x4;
+            pid = 0;
+          }
         }
       }
+      const int nb = min(kWave, my_steps - bstart);
+      auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
+      auto step_base = [&](int kk, const _Float16* pool) {
+        const int t0 = step_t0(kk);
+        const int pg = __builtin_amdgcn_readlane(pid, kk);
+        return pool + (((size_t)pg * Hkv + g) * P + (t0 % P)) * kHeadDim;
+      };
+      // Two steps in flight per wave in its ring (stage = step & 1), one in
+      // registers. Order of DMA issue: K(k+2) right after K(k) is read,
+      // V(k+2) right after V(k) is read, so before reading any half-step
+      // exactly three newer half-steps (24 operations) may be outstanding.
+      // Indices past the batch are clamped to its last step (a duplicate
+      // request that hits in cache) to keep that count exact.
+      const uint32_t ring_lds = lds_addr(ring) + lane * 16;
+      dma_k<0, 8>(step_base(0, kpool), ring, lane);
+      dma_v<0, 8>(step_base(0, vpool), ring + 8192, lane);
+      dma_k<0, 8>(step_base(min(1, nb - 1), kpool), ring + kRingStage, lane);
+      dma_v<0, 8>(step_base(min(1, nb - 1), vpool), ring + kRingStage + 8192, lane);
+      for (int kk = 0; kk < nb; ++kk) {
+        const int st = (kk & 1) * kRingStage;
+        const int t0 = step_t0(kk);
+        const int kn = min(kk + 2, nb - 1);
+        KFrag kf;
+        ring_read8<24, false>(kf.k, ring_lds + st);
+        dma_k<0, 8>(step_base(kn, kpool), ring + st, lane);
+        half4_t pb[RB];
+        step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, growbase, R, G, a.scale_log2);
+        VFrag vf;
+        ring_read8<24, false>(vf.v, ring_lds + st + 8192);
+        dma_v<0, 8>(step_base(kn, vpool), ring + st + 8192, lane);
+        step_pv<RB>(vf, pb, ws, lane, t0, kv);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    const int nb = min(kWave, my_steps - bstart);
-    auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
-    auto step_base = [&](int kk, const _Float16* pool) {
-      const int t0 = step_t0(kk);
-      const int pg = __builtin_amdgcn_readlane(pid, kk);
-      return pool + (((size_t)pg * Hkv + g) * P + (t0 % P)) * kHeadDim;
-    };
-    // One K and one V register buffer. The next step's K is requested as soon
-    // as the scores have consumed the current K, the next V as soon as the PV
-    // product has consumed the current V, so about one step per wave is in
-    // flight at any time. Loads are unconditional (the index is clamped; the
-    // duplicate request of the last step hits in cache) so the compiler waits
-    // for exactly the older buffer instead of draining every load.
-    KFrag kf;
-    VFrag vf;
-    load_k(kf, step_base(0, kpool), lane);
-    load_v(vf, step_base(0, vpool), lane);
-    for (int kk = 0; kk < nb; ++kk) {
-      const int t0 = step_t0(kk);
-      const int kn = min(kk + 1, nb - 1);
-      half4_t pb[RB];
-      step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, rowbase, R, G, a.scale_log2);
-      load_k(kf, step_base(kn, kpool), lane);
-      step_pv<RB>(vf, pb, ws, lane, t0, kv);
-      load_v(vf, step_base(kn, vpool), lane);
+  } else {
+    // ---- the two waves of a pair (same token steps, different rows) share
+    // a 3-stage ring: each issues half of every step's DMA blocks, and one
+    // workgroup barrier per half-step makes both halves visible. With three
+    // stages, the stage a DMA overwrites was last read one iteration ago, so
+    // the barrier before the current read also orders that reuse. All waves
+    // run the same number of iterations (the pair with fewer real steps
+    // repeats its last one without computing) so every barrier is reached.
+    constexpr int kStages = 3;
+    char* pring = reinterpret_cast<char*>(bigsm) + ts * kStages * kRingStage;
+    const uint32_t pring_lds = lds_addr(pring) + lane * 16;
+    const int all_steps = (n_steps + NTS - 1) / NTS;
+    int pid0 = ptab[chunk_lo / P];  // a valid page for pairs with nothing to do
+    if (pid0 < 0 || pid0 >= a.num_pages) {
+      flag_bits |= 0x4;
+      pid0 = 0;
+    }
+    pid0 = __builtin_amdgcn_readfirstlane(pid0);
+    for (int bstart = 0; bstart < all_steps; bstart += kWave) {
+      int pid = 0;
+      {
+        const int kl = bstart + lane;
+        if (kl < my_steps) {
+          const int t = chunk_lo + kStep * (ts + kl * NTS);
+          pid = ptab[t / P];
+          if (pid < 0 || pid >= a.num_pages) {
+            flag_bits |= 0x4;
+            pid = 0;
+          }
+        }
+      }
+      const int nb = min(kWave, all_steps - bstart);
+      const int valid = max(0, min(nb, my_steps - bstart));  // steps this pair computes
+      auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
+      auto step_base = [&](int kk, const _Float16* pool) {
+        if (valid == 0) return pool + (((size_t)pid0 * Hkv + g) * P + (chunk_lo % P)) * kHeadDim;
+        const int kc = min(kk, valid - 1);
+        const int t0 = step_t0(kc);
+        const int pg = __builtin_amdgcn_readlane(pid, kc);
+        return pool + (((size_t)pg * Hkv + g) * P + (t0 % P)) * kHeadDim;
+      };
+      auto stage = [&](int kk) { return (kk % kStages) * kRingStage; };
+      // each wave issues 4 of the 8 blocks of every half-step: 12 newer
+      // operations may be outstanding before a read
+      if (rg == 0) {
+        dma_k<0, 4>(step_base(0, kpool), pring + stage(0), lane);
+        dma_v<0, 4>(step_base(0, vpool), pring + stage(0) + 8192, lane);
+        dma_k<0, 4>(step_base(1, kpool), pring + stage(1), lane);
+        dma_v<0, 4>(step_base(1, vpool), pring + stage(1) + 8192, lane);
+      } else {
+        dma_k<4, 8>(step_base(0, kpool), pring + stage(0), lane);
+        dma_v<4, 8>(step_base(0, vpool), pring + stage(0) + 8192, lane);
+        dma_k<4, 8>(step_base(1, kpool), pring + stage(1), lane);
+        dma_v<4, 8>(step_base(1, vpool), pring + stage(1) + 8192, lane);
+      }
+      for (int kk = 0; kk < nb; ++kk) {
+        const int st = stage(kk), st2 = stage(kk + 2);
+        const int t0 = step_t0(kk);
+        const bool work = kk < valid;
+        KFrag kf;
+        ring_read8<12, true>(kf.k, pring_lds + st);
+        if (rg == 0) dma_k<0, 4>(step_base(kk + 2, kpool), pring + st2, lane);
+        else dma_k<4, 8>(step_base(kk + 2, kpool), pring + st2, lane);
+        half4_t pb[RB];
+        if (work) step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, growbase, R, G, a.scale_log2);
+        VFrag vf;
+        ring_read8<12, true>(vf.v, pring_lds + st + 8192);
+        if (rg == 0) dma_v<0, 4>(step_base(kk + 2, vpool), pring + st2 + 8192, lane);
+        else dma_v<4, 8>(step_base(kk + 2, vpool), pring + st2 + 8192, lane);
+        if (work) step_pv<RB>(vf, pb, ws, lane, t0, kv);
+      }
+      // drain, and keep the next batch's first DMAs off stages a slower wave
+      // may still be reading
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
   }
 
@@ -288,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
     }
   }
   if (flag_bits) atomicOr(&s_flag, flag_bits);
-  __syncthreads();  // every wave is past its main loop: Q area may be reused
+  __syncthreads();  // every wave is past its main loop: Q and ring space may be reused
 
   float lse_row[RB];
 #pragma unroll
@@ -307,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
     for (int j = 0; j < 16; ++j) ws.o[rb][j] *= f;
   }
 
-  float* obuf = reinterpret_cast<float*>(smem);
+  float* obuf = reinterpret_cast<float*>(bigsm);
   for (int k = 0; k < NTS; ++k) {
     if (ts == k) {
 #pragma unroll
@@ -341,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
   if (ts == 0 && hi == 0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int r = rowbase + rb * 16 + lo;
+      const int r = growbase + rb * 16 + lo;
       if (r < R) {
         const int i = r / G, j = r % G;
         const size_t orow = (size_t)(b * q_len + i) * Hq + g * G + j;
@@ -354,9 +544,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
     }
   }
   // rows out: 32 threads per row, 8 channels per thread
-  for (int r = tid / 32; r < R; r += kThreads / 32) {
+  const int rows_here = min(R - row0, NRG * RB * 16);
+  for (int lr = tid / 32; lr < rows_here; lr += kThreads / 32) {
+    const int r = row0 + lr;
     const int d0 = (tid % 32) * 8;
-    const float* src = obuf + r * kRowStride + d0;
+    const float* src = obuf + lr * kRowStride + d0;
     const float4 v0 = *reinterpret_cast<const float4*>(src);
     const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
     const int i = r / G, j = r % G;
@@ -374,10 +566,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
   if (tid == 0 && s_flag && a.flags) atomicOr(a.flags, s_flag);
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, int nrg, bool fp8, hipStream_t s) {
+void launch_verify_attention(const AttnArgs& a, int rb, int nrg, hipStream_t s) {
   dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
   dim3 block(kThreads);
-  (void)fp8;
   if (nrg == 1) {
     if (rb == 1) hipLaunchKernelGGL((verify_attn_f16_kernel<1, 1>), grid, block, 0, s, a);
     else if (rb == 2) hipLaunchKernelGGL((verify_attn_f16_kernel<2, 1>), grid, block, 0, s, a);
