@@ -121,7 +121,11 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     const long long target = (long long)kGroupsPerCU * cu_count();
     S = (target + groups - 1) / groups;
     long long chunk = (maxkv + S - 1) / S;
-    if (p->batch > 1 && chunk > kBatchChunkCap) chunk = kBatchChunkCap;
+    if (p->batch > 1 && chunk > kBatchChunkCap) {
+      // a whole multiple of the fill count keeps full rounds of workgroups
+      S *= (chunk + kBatchChunkCap - 1) / kBatchChunkCap;
+      chunk = (maxkv + S - 1) / S;
+    }
     if (chunk < kMinChunk) chunk = kMinChunk;
     S = (maxkv + chunk - 1) / chunk;
     if (S < 1) S = 1;
@@ -175,7 +179,8 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
   if (p->kv_dtype == SV_KV_FP8_E4M3) {
     if (!k_scales || !v_scales)
       return fail(SV_ERR_INVALID_ARGUMENT, "FP8 KV needs k_scales and v_scales");
-    return fail(SV_ERR_UNSUPPORTED, "FP8 E4M3 KV is not built yet");
+    if (pl.nrg != 1)
+      return fail(SV_ERR_UNSUPPORTED, "FP8 KV supports q_len * (num_q_heads/num_kv_heads) <= 48");
   } else if (k_scales || v_scales) {
     return fail(SV_ERR_INVALID_ARGUMENT, "k_scales/v_scales must be NULL for fp16 KV");
   }
@@ -213,7 +218,7 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
   a.chunk = pl.chunk;
   a.num_splits = pl.splits;
   a.scale_log2 = p->sm_scale * 1.44269504088896340736f;
-  sv::launch_verify_attention(a, pl.rb, pl.nrg, s);
+  sv::launch_verify_attention(a, pl.rb, pl.nrg, p->kv_dtype == SV_KV_FP8_E4M3, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
   if (pl.splits > 1) {

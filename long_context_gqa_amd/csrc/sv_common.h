@@ -60,7 +60,7 @@ __device__ inline int clamp_kv_len(int raw, int max_kv_len, int max_pages, int p
   return v;
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, int nrg, hipStream_t s);
+void launch_verify_attention(const AttnArgs& a, int rb, int nrg, bool fp8, hipStream_t s);
 void launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace sv

@@ -93,28 +93,17 @@ struct WaveState {
 };
 
 // Scores of one step, online-softmax update, and the fp16 P^T fragments.
+// Online-softmax update of one step from the scaled scores x (log2 units,
+// lane holds tokens t0 + 4*(lane/16) + i of row lane%16 in each row block):
+// causal/tail masking, the lazy reference, the running sum, and p.
 template <int RB>
-__device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __restrict__ qf,
-                                            WaveState<RB>& ws, half4_t (&pb)[RB], int lane, int t0,
-                                            int L, int kv, int rowbase, int R, int G,
-                                            float scale_log2) {
+__device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& ws, float (&p)[RB][4],
+                                             int lane, int t0, int L, int kv, int rowbase, int R,
+                                             int G) {
   const int lo = lane & 15, hi = lane >> 4;
   const bool tail = (t0 + kStep > L + 1);  // some key here is hidden from some row
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    // Q is re-read from LDS every step; the opaque offset keeps the compiler
-    // from hoisting 32*RB registers of fragments out of the loop.
-    int qo = rb * 8 * kWave + lane;
-    asm volatile("" : "+v"(qo));
-    u32x4 qv[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma_16x16x32(kf.k[s], qv[s], acc);
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = acc[i] * scale_log2;
     if (tail) {
       const int r = rowbase + rb * 16 + lo;
       int lim = kv;
@@ -122,14 +111,14 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
       const int tok = t0 + 4 * hi;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (tok + i >= lim) x[i] = -INFINITY;
+        if (tok + i >= lim) x[rb][i] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    float mx = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy reference: the row's reference m only moves when the tile max
     // exceeds it by more than kLazyLog2, so p = 2^(x - m) <= 2^kLazyLog2 stays
-    // well inside fp16 and the O/l rescale (192 accumulators) is rare.
+    // well inside fp16 and the O/l rescale (64*RB accumulators) is rare.
     // Numerator and denominator share the reference, so the result is the
     // same softmax.
     const bool bump = mx > ws.m[rb] + kLazyLog2;
@@ -142,11 +131,163 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
       ws.m[rb] = mnew;
     }
     const float ref = (ws.m[rb] == -INFINITY) ? 0.f : ws.m[rb];
-    float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[i] - ref);
-    ws.l[rb] += (p[0] + p[1]) + (p[2] + p[3]);
-    pb[rb] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    for (int i = 0; i < 4; ++i) p[rb][i] = exp2_fast(x[rb][i] - ref);
+    ws.l[rb] += (p[rb][0] + p[rb][1]) + (p[rb][2] + p[rb][3]);
+  }
+}
+
+// Scores of one fp16 step and the fp16 P^T fragments.
+template <int RB>
+__device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __restrict__ qf,
+                                            WaveState<RB>& ws, half4_t (&pb)[RB], int lane, int t0,
+                                            int L, int kv, int rowbase, int R, int G,
+                                            float scale_log2) {
+  float x[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Q is re-read from LDS every step; the opaque offset keeps the compiler
+    // from hoisting 32*RB registers of fragments out of the loop.
+    int qo = rb * 8 * kWave + lane;
+    asm volatile("" : "+v"(qo));
+    u32x4 qv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = mfma_16x16x32(kf.k[s], qv[s], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[rb][i] = acc[i] * scale_log2;
+  }
+  float p[RB][4];
+  softmax_step<RB>(x, ws, p, lane, t0, L, kv, rowbase, R, G);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    pb[rb] = half4_t{(_Float16)p[rb][0], (_Float16)p[rb][1], (_Float16)p[rb][2], (_Float16)p[rb][3]};
+}
+
+// ---- FP8 E4M3 steps -------------------------------------------------------
+//
+// E4M3 byte -> fp16 bit pattern whose value is the E4M3 value / 256: the sign
+// moves to bit 15 and exponent+mantissa (7 bits) land at bits 7..13, so the
+// fp16 exponent is the E4M3 exponent (bias 7 vs 15: a factor 2^-8) and
+// subnormals map to subnormals. Exact for every finite code; the factor 256
+// is folded into the per-block scales. Input: the two bytes placed at bits
+// 8..15 and 24..31 of t.
+__device__ __forceinline__ uint32_t e4m3_pair_to_f16(uint32_t t) {
+  return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
+}
+// bytes 0,1 and bytes 2,3 of w as two fp16 pairs (value / 256)
+__device__ __forceinline__ uint32_t e4m3_lo2(uint32_t w) {
+  return e4m3_pair_to_f16(((w << 8) & 0x0000FF00u) | ((w << 16) & 0xFF000000u));
+}
+__device__ __forceinline__ uint32_t e4m3_hi2(uint32_t w) {
+  return e4m3_pair_to_f16(((w >> 8) & 0x0000FF00u) | (w & 0xFF000000u));
+}
+// byte c of w0 and byte c of w1 as one fp16 pair (value / 256)
+__device__ __forceinline__ uint32_t e4m3_gather2(uint32_t w0, uint32_t w1, int c) {
+  const uint32_t b0 = (w0 >> (8 * c)) & 0xFFu, b1 = (w1 >> (8 * c)) & 0xFFu;
+  return e4m3_pair_to_f16((b0 << 8) | (b1 << 24));
+}
+
+// One FP8 step held by a wave.
+//   k[b]  : token lane%16, bytes 64b + 16*(lane/16) .. +16 (the 64-channel scale
+//           block b; MFMA k-steps 2b and 2b+1 take its halves)
+//   v[4e+bb]: token 4*(lane/16)+e, bytes 64bb + 4*(lane%16) .. +4
+//   sk[], sv[]: fp16 scales of tokens 4*(lane/16)+i, blocks 0..3 (i-major)
+struct KFrag8 {
+  u32x4 k[4];
+  u32x4 sk[2];
+  u32x4 sv[2];
+};
+struct VFrag8 {
+  uint32_t v[16];
+};
+
+__device__ __forceinline__ float half_at(const u32x4 (&h)[2], int idx) {
+  const uint32_t w = h[idx >> 3][(idx >> 1) & 3];
+  const uint16_t bits = (idx & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFFu);
+  return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+// Scores of one FP8 step: per 64-channel block, two MFMAs on the converted
+// K, then S = sum_b (256 * scale_b) * partial_b.
+template <int RB>
+__device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __restrict__ qf,
+                                             WaveState<RB>& ws, float (&p)[RB][4], int lane, int t0,
+                                             int L, int kv, int rowbase, int R, int G,
+                                             float scale_log2) {
+  u32x4 kc[8];
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk) {
+    kc[2 * bk] = u32x4{e4m3_lo2(kf.k[bk][0]), e4m3_hi2(kf.k[bk][0]), e4m3_lo2(kf.k[bk][1]),
+                       e4m3_hi2(kf.k[bk][1])};
+    kc[2 * bk + 1] = u32x4{e4m3_lo2(kf.k[bk][2]), e4m3_hi2(kf.k[bk][2]), e4m3_lo2(kf.k[bk][3]),
+                           e4m3_hi2(kf.k[bk][3])};
+  }
+  float fk[4][4];  // [token i][block]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * (256.f * scale_log2);
+  float x[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    int qo = rb * 8 * kWave + lane;
+    asm volatile("" : "+v"(qo));
+    u32x4 qv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[rb][i] = 0.f;
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_16x16x32(kc[2 * bk], qv[2 * bk], acc);
+      acc = mfma_16x16x32(kc[2 * bk + 1], qv[2 * bk + 1], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[rb][i] += fk[i][bk] * acc[i];
+    }
+  }
+  softmax_step<RB>(x, ws, p, lane, t0, L, kv, rowbase, R, G);
+}
+
+// O^T += V^T . P^T for one FP8 step: MFMA block j = 4*bb + c holds channels
+// 64*bb + 4*(lane%16) + c, all inside scale block bb, so the V scale (times
+// 256) is folded into P^T once per block group and V is used exactly.
+template <int RB>
+__device__ __forceinline__ void step_pv8(const VFrag8& vf, const KFrag8& kf, const float (&p)[RB][4],
+                                         WaveState<RB>& ws, int lane, int t0, int kv) {
+  const int hi = lane >> 4;
+  float fv[4][4];  // [token i][block]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) fv[i][bb] = half_at(kf.sv, 4 * i + bb) * 256.f;
+  // keys at or past kv_len: weight 0, and their (poison) scale must not enter
+  if (t0 + kStep > kv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t0 + 4 * hi + i >= kv) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) fv[i][bb] = 0.f;
+      }
+  }
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    half4_t pb[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      pb[rb] = half4_t{(_Float16)(p[rb][0] * fv[0][bb]), (_Float16)(p[rb][1] * fv[1][bb]),
+                       (_Float16)(p[rb][2] * fv[2][bb]), (_Float16)(p[rb][3] * fv[3][bb])};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t a0 = e4m3_gather2(vf.v[0 * 4 + bb], vf.v[1 * 4 + bb], c);
+      const uint32_t a1 = e4m3_gather2(vf.v[2 * 4 + bb], vf.v[3 * 4 + bb], c);
+      const int j = 4 * bb + c;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) ws.o[rb][j] = mfma_16x16x16(a0, a1, pb[rb], ws.o[rb][j]);
+    }
   }
 }
 
@@ -256,25 +397,102 @@ __device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) 
                                      SV_LP(ring + j * 1024), 16, 0, 0);
 }
 
+// FP8 ring stage: K bytes (4 KB), V bytes (4 KB), the step's K and V scales
+// (2 x 128 B, padded to 256).
+constexpr int kStage8 = 8448;
+
+// K half-step of an FP8 step: 4 blocks of 1 KB (lane l of block b = bytes
+// 64b + 16*(l/16) .. +16 of token l%16) and one 256-byte block holding the
+// 16 tokens' K scales (lanes 0..31) and V scales (lanes 32..63).
+__device__ __forceinline__ void dma_k8(const uint8_t* kb, const _Float16* ksb, const _Float16* vsb,
+                                       char* stage, int lane) {
+  const uint8_t* src = kb + (lane & 15) * kHeadDim + 16 * (lane >> 4);
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk)
+    __builtin_amdgcn_global_load_lds(SV_GP(src + 64 * bk), SV_LP(stage + bk * 1024), 16, 0, 0);
+  const _Float16* ssrc = lane < 32 ? ksb + 2 * lane : vsb + 2 * (lane - 32);
+  __builtin_amdgcn_global_load_lds(SV_GP(ssrc), SV_LP(stage + 8192), 4, 0, 0);
+}
+// V half-step of an FP8 step: 16 blocks of 256 B, block 4e+bb lane l = bytes
+// 64bb + 4*(l%16) .. +4 of token 4*(l/16)+e.
+__device__ __forceinline__ void dma_v8(const uint8_t* vb, char* stage, int lane) {
+  const uint8_t* src = vb + (4 * (lane >> 4)) * kHeadDim + 4 * (lane & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+      __builtin_amdgcn_global_load_lds(SV_GP(src + e * kHeadDim + 64 * bb),
+                                       SV_LP(stage + 4096 + (4 * e + bb) * 256), 4, 0, 0);
+}
+
+template <int VMCNT>
+__device__ __forceinline__ void ring_read_k8(KFrag8& f, uint32_t addr_lane, uint32_t addr_scale) {
+  asm volatile(
+      "s_waitcnt vmcnt(%10)\n\t"
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "ds_read_b128 %5, %9 offset:16\n\t"
+      "ds_read_b128 %6, %9 offset:128\n\t"
+      "ds_read_b128 %7, %9 offset:144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(f.k[0]), "=v"(f.k[1]), "=v"(f.k[2]), "=v"(f.k[3]), "=v"(f.sk[0]), "=v"(f.sk[1]),
+        "=v"(f.sv[0]), "=v"(f.sv[1])
+      : "v"(addr_lane), "v"(addr_scale), "n"(VMCNT)
+      : "memory");
+}
+
+template <int VMCNT>
+__device__ __forceinline__ void ring_read_v8(VFrag8& f, uint32_t addr) {
+  asm volatile(
+      "s_waitcnt vmcnt(%17)\n\t"
+      "ds_read_b32 %0, %16\n\t"
+      "ds_read_b32 %1, %16 offset:256\n\t"
+      "ds_read_b32 %2, %16 offset:512\n\t"
+      "ds_read_b32 %3, %16 offset:768\n\t"
+      "ds_read_b32 %4, %16 offset:1024\n\t"
+      "ds_read_b32 %5, %16 offset:1280\n\t"
+      "ds_read_b32 %6, %16 offset:1536\n\t"
+      "ds_read_b32 %7, %16 offset:1792\n\t"
+      "ds_read_b32 %8, %16 offset:2048\n\t"
+      "ds_read_b32 %9, %16 offset:2304\n\t"
+      "ds_read_b32 %10, %16 offset:2560\n\t"
+      "ds_read_b32 %11, %16 offset:2816\n\t"
+      "ds_read_b32 %12, %16 offset:3072\n\t"
+      "ds_read_b32 %13, %16 offset:3328\n\t"
+      "ds_read_b32 %14, %16 offset:3584\n\t"
+      "ds_read_b32 %15, %16 offset:3840\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(f.v[0]), "=v"(f.v[1]), "=v"(f.v[2]), "=v"(f.v[3]), "=v"(f.v[4]), "=v"(f.v[5]),
+        "=v"(f.v[6]), "=v"(f.v[7]), "=v"(f.v[8]), "=v"(f.v[9]), "=v"(f.v[10]), "=v"(f.v[11]),
+        "=v"(f.v[12]), "=v"(f.v[13]), "=v"(f.v[14]), "=v"(f.v[15])
+      : "v"(addr), "n"(VMCNT)
+      : "memory");
+}
+
 constexpr int kRingStage = 16384;               // K (8 KB) + V (8 KB) of one step
 constexpr int kRingPerWave = 2 * kRingStage;    // two stages per wave
 
-template <int RB, int NRG>
+template <int RB, int NRG, bool FP8>
 struct Smem {
   static constexpr int NTS = kWavesPerGroup / NRG;
   static constexpr int QBYTES = NRG * RB * 8 * kWave * 16;
   static constexpr int OBYTES = NRG * RB * 16 * kRowStride * 4;
   // NRG 1: a private 2-stage ring per wave; NRG 2: a 3-stage ring per pair
-  static constexpr int RBYTES = NRG == 1 ? kWavesPerGroup * kRingPerWave : NTS * 3 * kRingStage;
+  static constexpr int RBYTES = FP8 ? kWavesPerGroup * 2 * kStage8
+                               : (NRG == 1 ? kWavesPerGroup * kRingPerWave : NTS * 3 * kRingStage);
   // Q fragments in their own array (so reading them never waits for the
   // ring's DMAs); the ring and, after the main loop, the combine buffer
   // share the second array.
   static constexpr int BIG = RBYTES > OBYTES ? RBYTES : OBYTES;
 };
 
-template <int RB, int NRG>
-__global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a) {
-  using SM = Smem<RB, NRG>;
+template <int RB, int NRG, bool FP8>
+__global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
+  static_assert(!FP8 || NRG == 1, "FP8 KV is built for up to 48 rows per KV head");
+  using SM = Smem<RB, NRG, FP8>;
   constexpr int NTS = SM::NTS;   // waves sharing one row group
   __shared__ __attribute__((aligned(1024))) unsigned char qsm[SM::QBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char bigsm[SM::BIG];
@@ -311,8 +529,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < R) {
       const int i = r / G, j = r % G;
-      const _Float16* src =
-          a.q + ((size_t)(b * q_len + i) * Hq + g * G + j) * kHeadDim + 32 * s + 8 * (ln >> 4);
+      // channel map of the score MFMA's k-step s: fp16 KV 32s + 8*(lane/16);
+      // FP8 KV 64*(s/2) + 16*(lane/16) + 8*(s%2) (two k-steps per scale block)
+      const int d0 = FP8 ? 64 * (s >> 1) + 16 * (ln >> 4) + 8 * (s & 1) : 32 * s + 8 * (ln >> 4);
+      const _Float16* src = a.q + ((size_t)(b * q_len + i) * Hq + g * G + j) * kHeadDim + d0;
       v = *reinterpret_cast<const u32x4*>(src);
     }
     qlds[idx] = v;
@@ -337,7 +557,62 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
   const _Float16* kpool = static_cast<const _Float16*>(a.k_pages);
   const _Float16* vpool = static_cast<const _Float16*>(a.v_pages);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
-  if constexpr (NRG == 1) {
+  if constexpr (FP8) {
+    // ---- FP8: each wave owns its token steps and a private 2-stage ring ----
+    // (same schedule as the fp16 ring below; half-steps are K bytes + both
+    // scale sets (5 operations) and V bytes (16 operations))
+    char* ring = reinterpret_cast<char*>(bigsm) + wave * 2 * kStage8;
+    const uint8_t* kpool8 = static_cast<const uint8_t*>(a.k_pages);
+    const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
+    const uint32_t ring_lds = lds_addr(ring);
+    for (int bstart = 0; bstart < my_steps; bstart += kWave) {
+      int pid = 0;
+      {
+        const int kl = bstart + lane;
+        if (kl < my_steps) {
+          const int t = chunk_lo + kStep * (ts + kl * NTS);
+          pid = ptab[t / P];
+          if (pid < 0 || pid >= a.num_pages) {
+            flag_bits |= 0x4;
+            pid = 0;
+          }
+        }
+      }
+      const int nb = min(kWave, my_steps - bstart);
+      auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
+      auto tok_row = [&](int kk) {  // (page, KV head, slot) row index of the step's first token
+        const int pg = __builtin_amdgcn_readlane(pid, kk);
+        return ((size_t)pg * Hkv + g) * P + (step_t0(kk) % P);
+      };
+      auto issue_k = [&](int kk, int stg) {
+        const size_t tr = tok_row(kk);
+        dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring + stg * kStage8, lane);
+      };
+      auto issue_v = [&](int kk, int stg) {
+        dma_v8(vpool8 + tok_row(kk) * kHeadDim, ring + stg * kStage8, lane);
+      };
+      issue_k(0, 0);
+      issue_v(0, 0);
+      issue_k(min(1, nb - 1), 1);
+      issue_v(min(1, nb - 1), 1);
+      for (int kk = 0; kk < nb; ++kk) {
+        const int st = kk & 1;
+        const int t0 = step_t0(kk);
+        const int kn = min(kk + 2, nb - 1);
+        const uint32_t sbase = ring_lds + st * kStage8;
+        KFrag8 kf;
+        ring_read_k8<37>(kf, sbase + lane * 16, sbase + 8192 + 32 * (lane >> 4));
+        issue_k(kn, st);
+        float pr[RB][4];
+        step_scores8<RB>(kf, qf, ws, pr, lane, t0, L, kv, growbase, R, G, a.scale_log2);
+        VFrag8 vf;
+        ring_read_v8<26>(vf, sbase + 4096 + lane * 4);
+        issue_v(kn, st);
+        step_pv8<RB>(vf, kf, pr, ws, lane, t0, kv);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  } else if constexpr (NRG == 1) {
     // ---- each wave owns its token steps and a private 2-stage LDS ring ----
     char* ring = reinterpret_cast<char*>(bigsm) + wave * kRingPerWave;
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
@@ -503,22 +778,40 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float* rowp = obuf + (rowbase + rb * 16 + lo) * kRowStride;
+        // O^T block j of lane (hi, lo) holds channel rows 4*hi + i of row lo:
+        // fp16 KV block j = 8h + c is channels 128h + 8*(4*hi+i) + c;
+        // FP8 KV block j = 4bb + c is channels 64bb + 4*(4*hi+i) + c
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float4* dst = reinterpret_cast<float4*>(rowp + 128 * h + 32 * hi + 8 * i);
-            float4 v0 = make_float4(ws.o[rb][8 * h + 0][i], ws.o[rb][8 * h + 1][i],
-                                    ws.o[rb][8 * h + 2][i], ws.o[rb][8 * h + 3][i]);
-            float4 v1 = make_float4(ws.o[rb][8 * h + 4][i], ws.o[rb][8 * h + 5][i],
-                                    ws.o[rb][8 * h + 6][i], ws.o[rb][8 * h + 7][i]);
-            if (k == 0) {
-              dst[0] = v0;
-              dst[1] = v1;
+            float4 v0, v1;
+            float* d0p;
+            float* d1p;
+            if constexpr (FP8) {
+              v0 = make_float4(ws.o[rb][8 * h + 0][i], ws.o[rb][8 * h + 1][i], ws.o[rb][8 * h + 2][i],
+                               ws.o[rb][8 * h + 3][i]);
+              v1 = make_float4(ws.o[rb][8 * h + 4][i], ws.o[rb][8 * h + 5][i], ws.o[rb][8 * h + 6][i],
+                               ws.o[rb][8 * h + 7][i]);
+              d0p = rowp + 64 * (2 * h) + 16 * hi + 4 * i;
+              d1p = rowp + 64 * (2 * h + 1) + 16 * hi + 4 * i;
             } else {
-              float4 a0 = dst[0], a1 = dst[1];
-              dst[0] = make_float4(a0.x + v0.x, a0.y + v0.y, a0.z + v0.z, a0.w + v0.w);
-              dst[1] = make_float4(a1.x + v1.x, a1.y + v1.y, a1.z + v1.z, a1.w + v1.w);
+              v0 = make_float4(ws.o[rb][8 * h + 0][i], ws.o[rb][8 * h + 1][i], ws.o[rb][8 * h + 2][i],
+                               ws.o[rb][8 * h + 3][i]);
+              v1 = make_float4(ws.o[rb][8 * h + 4][i], ws.o[rb][8 * h + 5][i], ws.o[rb][8 * h + 6][i],
+                               ws.o[rb][8 * h + 7][i]);
+              d0p = rowp + 128 * h + 32 * hi + 8 * i;
+              d1p = d0p + 4;
+            }
+            float4* q0 = reinterpret_cast<float4*>(d0p);
+            float4* q1 = reinterpret_cast<float4*>(d1p);
+            if (k == 0) {
+              *q0 = v0;
+              *q1 = v1;
+            } else {
+              const float4 a0 = *q0, a1 = *q1;
+              *q0 = make_float4(a0.x + v0.x, a0.y + v0.y, a0.z + v0.z, a0.w + v0.w);
+              *q1 = make_float4(a1.x + v1.x, a1.y + v1.y, a1.z + v1.z, a1.w + v1.w);
             }
           }
         }
@@ -566,15 +859,19 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_f16_kernel(AttnArgs a
   if (tid == 0 && s_flag && a.flags) atomicOr(a.flags, s_flag);
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, int nrg, hipStream_t s) {
+void launch_verify_attention(const AttnArgs& a, int rb, int nrg, bool fp8, hipStream_t s) {
   dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
   dim3 block(kThreads);
-  if (nrg == 1) {
-    if (rb == 1) hipLaunchKernelGGL((verify_attn_f16_kernel<1, 1>), grid, block, 0, s, a);
-    else if (rb == 2) hipLaunchKernelGGL((verify_attn_f16_kernel<2, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((verify_attn_f16_kernel<3, 1>), grid, block, 0, s, a);
+  if (fp8) {
+    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, 1, true>), grid, block, 0, s, a);
+    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, 1, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_attn_kernel<3, 1, true>), grid, block, 0, s, a);
+  } else if (nrg == 1) {
+    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, 1, false>), grid, block, 0, s, a);
+    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, 1, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_attn_kernel<3, 1, false>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((verify_attn_f16_kernel<3, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((verify_attn_kernel<3, 2, false>), grid, block, 0, s, a);
   }
 }
 

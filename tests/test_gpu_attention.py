@@ -146,3 +146,76 @@ def test_bad_page_ids_and_lengths_are_flagged_and_clamped():
     kv[1] = 400  # above the host bound max_kv_len
     out, lse, flags = run_gpu(x, kv_lens=kv, max_kv_len=300)
     assert flags & 1
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 KV with per-token, per-KV-head fp16 scales over 64-channel blocks
+
+@pytest.mark.parametrize("variant", ["unit", "literal"])
+@pytest.mark.parametrize("B,q_len,lens,P", [
+    (1, 1, [77], 16),
+    (1, 8, [8], 16),
+    (2, 8, [333, 1290], 16),
+    (3, 5, [17, 160, 1025], 64),
+    (1, 8, [5000], 32),
+])
+def test_fp8_small_parity(B, q_len, lens, P, variant):
+    x = case(B, q_len, lens, P, variant, seed=B * 31 + q_len, kv_dtype="fp8_e4m3")
+    ref, ref_lse = oracle(x)
+    for splits in (0, 1, 3):
+        say(f"fp8 B={B} q={q_len} lens={lens} P={P} {variant} splits={splits}")
+        out, lse, flags = run_gpu(x, num_splits=splits)
+        assert flags == 0
+        check(out, lse, ref, ref_lse, what=f"fp8 splits={splits}")
+
+
+def test_fp8_every_code_is_decoded_exactly():
+    # K and V cycle through every finite E4M3 code (subnormals included) with
+    # random scales; the oracle decodes from the format definition
+    x = case(1, 8, [1200], 16, "unit", seed=77, kv_dtype="fp8_e4m3")
+    g = torch.Generator().manual_seed(5)
+    codes = torch.tensor([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=torch.uint8)
+    n = x.k_pages.numel()
+    kc = codes[torch.randint(0, len(codes), (n,), generator=g)].view(x.k_pages.shape)
+    vc = codes[torch.arange(n) % len(codes)].view(x.v_pages.shape)
+    x.k_pages = kc.cuda()
+    x.v_pages = vc.cuda()
+    ks = (torch.rand(x.k_scales.shape, generator=g) * 0.004 + 1e-4).to(torch.float16)
+    vs = (torch.rand(x.v_scales.shape, generator=g) * 0.004 + 1e-4).to(torch.float16)
+    x.k_scales, x.v_scales = ks.cuda(), vs.cuda()
+    ref, ref_lse = oracle(x)
+    out, lse, _ = run_gpu(x, num_splits=2)
+    check(out, lse, ref, ref_lse, what="fp8 every code")
+
+
+def test_fp8_one_hot_probe_is_exact():
+    # one key per KV head equal to the query direction; the output row must be
+    # the dequantised V row of that key exactly (its fp16 rounding)
+    L, q_len, P = 200, 8, 16
+    x = case(1, q_len, [L + q_len], P, "unit", seed=3, kv_dtype="fp8_e4m3")
+    g = torch.Generator().manual_seed(6)
+    u = (torch.randint(0, 2, (4, 256), generator=g) * 2 - 1).to(torch.float16)
+    x.q.copy_((8 * u).repeat_interleave(6, 0).unsqueeze(0).expand(q_len, 24, 256).cuda())
+    kp = torch.zeros_like(x.k_pages)
+    ks = torch.ones_like(x.k_scales)
+    pt = x.page_table[0]
+    t_star = 123
+    code8 = torch.where(u > 0, torch.tensor(0x48, dtype=torch.uint8), torch.tensor(0xC8, dtype=torch.uint8))  # +-4
+    for gq in range(4):
+        kp[int(pt[t_star // P]), gq, t_star % P] = code8[gq].cuda()
+    x.k_pages, x.k_scales = kp, ks
+    out, lse, _ = run_gpu(x)
+    ref, ref_lse = oracle(x)
+    check(out, lse, ref, ref_lse, what="fp8 probe")
+    for i in range(q_len):
+        for gq in range(4):
+            want = ref[i, 6 * gq].astype(np.float16).astype(np.float32)
+            assert np.array_equal(out[i, 6 * gq], want)
+
+
+def test_fp8_more_than_48_rows_is_rejected():
+    from long_context_gqa_amd import binding as B
+    x = case(1, 16, [100], 16, "unit", seed=1, kv_dtype="fp8_e4m3")
+    with pytest.raises(B.SvError) as e:
+        run_gpu(x)
+    assert e.value.status == B.SV_ERR_UNSUPPORTED

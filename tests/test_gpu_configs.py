@@ -30,7 +30,7 @@ def sample_groups(wl, kv_lens):
 
 
 @pytest.mark.parametrize("variant", ["literal", "unit"])
-@pytest.mark.parametrize("wl_id", [1, 2, 3, 4])
+@pytest.mark.parametrize("wl_id", [1, 2, 3, 4, 5])
 def test_full_size_config(wl_id, variant):
     wl = W.WORKLOADS[wl_id]
     say(f"config {wl_id} {wl.name} {variant}: generating")
