@@ -123,7 +123,7 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     long long chunk = (maxkv + S - 1) / S;
     if (p->batch > 1 && chunk > kBatchChunkCap) {
       // a whole multiple of the fill count keeps full rounds of workgroups
-      S *= (chunk + kBatchChunkCap - 1) / kBatchChunkCap;
+      S *= chunk / kBatchChunkCap;
       chunk = (maxkv + S - 1) / S;
     }
     if (chunk < kMinChunk) chunk = kMinChunk;
