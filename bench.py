@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per verify_attn launch (FETCH+WRITE)")
+                    help="JSON with measured HBM bytes per verify_attn launch (default: the one under "
+                         "profiles/ for this workload, used only while the kernel source is unchanged)")
     return ap.parse_args()
 
 
@@ -155,10 +156,7 @@ def main():
     kern_gbs = attn_bytes / (kern_us * 1e-6) / 1e9
     rows = wl.batch * wl.q_len
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic, wl.name)
 
     sweep = None
     if args.sweep_splits:
@@ -215,7 +213,7 @@ def main():
             "algorithmic_bytes": acc_bytes,
         },
         "roofline": {
-            "kernel": "verify_attn_f16_kernel",
+            "kernel": "verify_attn_kernel",
             "bound": "hbm",
             "achieved": round(kern_gbs, 1),
             "peak": PEAK_HBM_GBS,
@@ -230,6 +228,22 @@ def main():
         "split_sweep": sweep,
     }
     print(json.dumps(res), flush=True)
+
+
+def measured_traffic(path, workload):
+    """HBM bytes (FETCH + WRITE) per verify_attn launch from the rocprofv3
+    counter runs recorded under profiles/, or None when there is no record for
+    this workload or the kernel source has changed since it was taken."""
+    import hashlib
+    path = path or os.path.join(ROOT, "profiles", f"traffic_verify_attn_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
 def cpu_baseline(x, wl):

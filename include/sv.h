@@ -64,7 +64,7 @@ typedef struct {
   int32_t num_q_heads;       /* Hq; query head h uses KV head h / (Hq/Hkv) */
   int32_t num_kv_heads;      /* Hkv, divides Hq; q_len * Hq/Hkv <= 96 (<= 48 for FP8 KV) */
   int32_t head_dim;          /* D, must be 256 */
-  int32_t page_size;         /* P tokens per page: 16, 32 or 64 */
+  int32_t page_size;         /* P tokens per page: a multiple of 16, at most 4096 */
   int32_t num_pages;         /* pages in the pool (bounds page ids) */
   int32_t max_pages_per_req; /* row stride of page_table */
   int32_t max_kv_len;        /* host upper bound on every kv_lens[b]; sizes the grid */
