@@ -2,13 +2,13 @@
 // then the longest prefix of drafts that match, the bonus token and the new
 // cache length.
 //
-// Stage 1 (argmax_partial): one workgroup per (row, slice of the vocabulary);
-//   every thread walks its float4 columns in increasing order, so the
-//   per-thread winner already prefers the lowest index; winners are combined
-//   with the rule "larger value, then lower index" across the wave (shuffles)
-//   and across the 4 waves (LDS). Output (value, index) per (row, slice).
-// Stage 2 (accept_finalize): one wave per request combines the slices of its
-//   q_len rows with the same rule and walks the drafts.
+// Stage 1 (argmax_partial): one workgroup per (row, slice of 8,192 columns);
+//   every thread issues all of its float4 loads first, then keeps the winner
+//   under the rule "larger value, then lower index"; winners are combined
+//   with the same rule across the wave (shuffles) and across the 4 waves
+//   (LDS). Output (value, index) per (row, slice).
+// Stage 2 (accept_finalize): one workgroup per request reduces the slices of
+//   all its q_len rows at once (a team of lanes per row) and walks the drafts.
 // The logits are read once; the scan is HBM-bound.
 #include <stdint.h>
 
@@ -52,13 +52,23 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* _
   const float* rp = logits + (size_t)row * vocab;
   Best b{-INFINITY, INT32_MAX};
   if (VEC4) {
-    // columns [lo, hi) with lo, hi multiples of 4 (vocab % 4 == 0)
-    for (int c = lo + 4 * threadIdx.x; c < hi; c += 4 * kThreads) {
-      const float4 v = *reinterpret_cast<const float4*>(rp + c);
-      b = better(b, Best{v.x, c});
-      b = better(b, Best{v.y, c + 1});
-      b = better(b, Best{v.z, c + 2});
-      b = better(b, Best{v.w, c + 3});
+    // columns [lo, hi) with lo, hi multiples of 4 (vocab % 4 == 0); all of a
+    // thread's loads are issued before any is used
+    constexpr int kPer = kAcceptSlice / (4 * kThreads);
+    float4 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = lo + 4 * (threadIdx.x + u * kThreads);
+      v[u] = c < hi ? *reinterpret_cast<const float4*>(rp + c)
+                    : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = lo + 4 * (threadIdx.x + u * kThreads);
+      b = better(b, Best{v[u].x, c});
+      b = better(b, Best{v[u].y, c + 1});
+      b = better(b, Best{v[u].z, c + 2});
+      b = better(b, Best{v[u].w, c + 3});
     }
   } else {
     for (int c = lo + threadIdx.x; c < hi; c += kThreads) b = better(b, Best{rp[c], c});
@@ -75,37 +85,46 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* _
   }
 }
 
-__global__ __launch_bounds__(kWave) void accept_finalize_kernel(
+// One workgroup per request: the slices of all q_len rows are reduced at
+// once (each row by a team of lanes), then one thread walks the drafts.
+__global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
     const float2* __restrict__ ws, int n_slices, const int32_t* __restrict__ draft_ids, int q_len,
     int32_t* accept_len, int32_t* bonus_ids, int32_t* argmax_ids, const int32_t* kv_lens_in,
     int32_t* kv_lens_out) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  int acc = 0;
-  bool open = true;  // still matching
-  int bonus = 0;
-  for (int j = 0; j < q_len; ++j) {
-    const size_t row = (size_t)b * q_len + j;
+  __shared__ int am_s[kMaxAcceptRows];
+  __shared__ Best red[kThreads];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  // team of lanes per row: the largest power of two with q_len teams <= 256
+  int team = kThreads;
+  while (team > 1 && team * q_len > kThreads) team >>= 1;
+  for (int j0 = 0; j0 < q_len; j0 += kThreads / team) {
+    const int j = j0 + tid / team, k = tid % team;
     Best x{-INFINITY, INT32_MAX};
-    for (int s = lane; s < n_slices; s += kWave) {
-      const float2 p = ws[row * n_slices + s];
-      x = better(x, Best{p.x, __float_as_int(p.y)});
-    }
-    x = wave_best(x);
-    const int am = (x.i == INT32_MAX) ? 0 : x.i;
-    if (argmax_ids && lane == 0) argmax_ids[row] = am;
-    if (open) {
-      if (j < q_len - 1 && draft_ids[(size_t)b * (q_len - 1) + j] == am) {
-        ++acc;
-      } else {
-        open = false;
-        bonus = am;
-        if (!argmax_ids) break;
+    if (j < q_len) {
+      const size_t row = (size_t)b * q_len + j;
+      for (int s = k; s < n_slices; s += team) {
+        const float2 p = ws[row * n_slices + s];
+        x = better(x, Best{p.x, __float_as_int(p.y)});
       }
     }
+    red[tid] = x;
+    __syncthreads();
+    for (int w = team / 2; w > 0; w >>= 1) {
+      if (k < w) red[tid] = better(red[tid], red[tid + w]);
+      __syncthreads();
+    }
+    if (k == 0 && j < q_len) {
+      const int am = (red[tid].i == INT32_MAX) ? 0 : red[tid].i;
+      am_s[j] = am;
+      if (argmax_ids) argmax_ids[(size_t)b * q_len + j] = am;
+    }
+    __syncthreads();
   }
-  if (lane == 0) {
+  if (tid == 0) {
+    int acc = 0;
+    while (acc < q_len - 1 && draft_ids[(size_t)b * (q_len - 1) + acc] == am_s[acc]) ++acc;
     accept_len[b] = acc;
-    bonus_ids[b] = bonus;
+    bonus_ids[b] = am_s[acc];
     if (kv_lens_out) kv_lens_out[b] = kv_lens_in[b] - q_len + 1 + acc;
   }
 }
@@ -118,7 +137,7 @@ void launch_greedy_accept(const AcceptLaunch& a, hipStream_t s) {
   else
     hipLaunchKernelGGL((argmax_partial_kernel<false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
                        a.slice, a.n_slices, a.ws);
-  hipLaunchKernelGGL(accept_finalize_kernel, dim3(a.batch), dim3(kWave), 0, s, a.ws, a.n_slices,
+  hipLaunchKernelGGL(accept_finalize_kernel, dim3(a.batch), dim3(kThreads), 0, s, a.ws, a.n_slices,
                      a.draft_ids, a.q_len, a.accept_len, a.bonus_ids, a.argmax_ids, a.kv_lens_in,
                      a.kv_lens_out);
 }

@@ -19,6 +19,7 @@ struct AcceptLaunch {
 };
 
 constexpr int kAcceptSlice = 8192;  // vocabulary columns per argmax workgroup
+constexpr int kMaxAcceptRows = 1024;  // largest q_len sv_greedy_accept takes
 
 void launch_greedy_accept(const AcceptLaunch& a, hipStream_t s);
 

@@ -288,6 +288,8 @@ sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_
     return fail(SV_ERR_INVALID_ARGUMENT, "batch, q_len and vocab must be >= 1");
   if ((long long)batch * q_len > 65535)
     return fail(SV_ERR_UNSUPPORTED, "batch * q_len must be <= 65535");
+  if (q_len > sv::kMaxAcceptRows)
+    return fail(SV_ERR_UNSUPPORTED, "q_len must be <= %d", sv::kMaxAcceptRows);
   if (!logits || !accept_len || !bonus_ids)
     return fail(SV_ERR_INVALID_ARGUMENT, "logits, accept_len and bonus_ids must be non-NULL");
   if (q_len > 1 && !draft_ids) return fail(SV_ERR_INVALID_ARGUMENT, "draft_ids is NULL");

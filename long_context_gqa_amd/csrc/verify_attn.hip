@@ -337,109 +337,132 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #define SV_GP(p) ((__attribute__((address_space(1))) void*)(p))
 #define SV_LP(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Eight 16-byte reads from one 8 KB ring block after waiting until at most
-// VMCNT of this wave's vector-memory operations (the newer half-steps) are
-// outstanding, i.e. until the block's own DMA has landed; with BARRIER the
-// workgroup also meets, so blocks DMA-ed by the partner wave have landed too.
-template <int VMCNT, bool BARRIER>
+// Outputs are early-clobber: a destination must not share a register with
+// the address, which later reads of the same block still use while earlier
+// ones may already have returned.
+// Eight 16-byte reads at addr, addr + STRIDE, ..., addr + 7*STRIDE after
+// waiting until at most VMCNT of this wave's vector-memory operations (the
+// newer half-steps) are outstanding, i.e. until the block's own DMA has
+// landed; with BARRIER the workgroup also meets, so blocks DMA-ed by the
+// partner wave have landed too.
+template <int VMCNT, bool BARRIER, int STRIDE>
 __device__ __forceinline__ void ring_read8(u32x4 (&d)[8], uint32_t addr) {
   if constexpr (BARRIER) {
     asm volatile(
         "s_waitcnt vmcnt(%9)\n\t"
         "s_barrier\n\t"
         "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %8 offset:3072\n\t"
-        "ds_read_b128 %4, %8 offset:4096\n\t"
-        "ds_read_b128 %5, %8 offset:5120\n\t"
-        "ds_read_b128 %6, %8 offset:6144\n\t"
-        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %8 offset:%14\n\t"
+        "ds_read_b128 %6, %8 offset:%15\n\t"
+        "ds_read_b128 %7, %8 offset:%16\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(d[0]), "=v"(d[1]), "=v"(d[2]), "=v"(d[3]), "=v"(d[4]), "=v"(d[5]), "=v"(d[6]), "=v"(d[7])
-        : "v"(addr), "n"(VMCNT)
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+        : "v"(addr), "n"(VMCNT), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE), "n"(4 * STRIDE),
+          "n"(5 * STRIDE), "n"(6 * STRIDE), "n"(7 * STRIDE)
         : "memory");
   } else {
     asm volatile(
         "s_waitcnt vmcnt(%9)\n\t"
         "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %8 offset:3072\n\t"
-        "ds_read_b128 %4, %8 offset:4096\n\t"
-        "ds_read_b128 %5, %8 offset:5120\n\t"
-        "ds_read_b128 %6, %8 offset:6144\n\t"
-        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %8 offset:%14\n\t"
+        "ds_read_b128 %6, %8 offset:%15\n\t"
+        "ds_read_b128 %7, %8 offset:%16\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(d[0]), "=v"(d[1]), "=v"(d[2]), "=v"(d[3]), "=v"(d[4]), "=v"(d[5]), "=v"(d[6]), "=v"(d[7])
-        : "v"(addr), "n"(VMCNT)
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+        : "v"(addr), "n"(VMCNT), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE), "n"(4 * STRIDE),
+          "n"(5 * STRIDE), "n"(6 * STRIDE), "n"(7 * STRIDE)
         : "memory");
   }
 }
 
-// Direct HBM -> LDS copies of 1 KB blocks [B0, B1) of one half-step: lane l
-// of block j lands at ring + j*1024 + 16*l (the order the MFMA operand reads
-// it). K block j = channels 32j + 8*(lane/16) of token lane%16; V block 2e+h
-// = channels 128h + 8*(lane%16) of token 4*(lane/16)+e.
+// Direct HBM -> LDS copies of 1 KB blocks [B0, B1) of one half-step; block j
+// is tokens 2j and 2j+1 of the (page, KV head) run, read contiguously (lane l
+// lands at ring + j*1024 + 16*l). V is stored as is: token t, 16-byte chunk c
+// at t*512 + 16c. K's chunks are permuted inside each token row: chunk c of
+// token t sits at position c ^ (t & 3), so that the MFMA operand reads (lane =
+// token t, chunk 4s + lane/16) of 16 lanes spread over the LDS banks.
 template <int B0, int B1>
 __device__ __forceinline__ void dma_k(const _Float16* kb, char* ring, int lane) {
-  const _Float16* src = kb + (lane & 15) * kHeadDim + 8 * (lane >> 4);
 #pragma unroll
-  for (int s = B0; s < B1; ++s)
-    __builtin_amdgcn_global_load_lds(SV_GP(src + 32 * s), SV_LP(ring + s * 1024), 16, 0, 0);
+  for (int j = B0; j < B1; ++j) {
+    const int t = 2 * j + (lane >> 5);
+    const int c = (lane & 31) ^ (t & 3);
+    __builtin_amdgcn_global_load_lds(SV_GP(kb + t * kHeadDim + 8 * c), SV_LP(ring + j * 1024), 16, 0, 0);
+  }
 }
 template <int B0, int B1>
 __device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) {
-  const _Float16* src = vb + (4 * (lane >> 4)) * kHeadDim + 8 * (lane & 15);
 #pragma unroll
   for (int j = B0; j < B1; ++j)
-    __builtin_amdgcn_global_load_lds(SV_GP(src + (j >> 1) * kHeadDim + 128 * (j & 1)),
-                                     SV_LP(ring + j * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(SV_GP(vb + (j * kWave + lane) * 8), SV_LP(ring + j * 1024), 16, 0, 0);
 }
+// Per-lane ring offsets of the operand reads. K: lane (token l%16, group
+// l/16) reads k-step s at k_lane_off + 64*s. V: fragment 2e+h (token
+// 4*(l/16)+e, channels 128h + 8*(l%16)) at v_lane_off + 256*(2e+h).
+__device__ __forceinline__ uint32_t k_lane_off(int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  return t * 512 + 16 * (g ^ (t & 3));
+}
+__device__ __forceinline__ uint32_t v_lane_off(int lane) { return (lane >> 4) * 2048 + (lane & 15) * 16; }
 
 // FP8 ring stage: K bytes (4 KB), V bytes (4 KB), the step's K and V scales
 // (2 x 128 B, padded to 256).
 constexpr int kStage8 = 8448;
 
-// K half-step of an FP8 step: 4 blocks of 1 KB (lane l of block b = bytes
-// 64b + 16*(l/16) .. +16 of token l%16) and one 256-byte block holding the
-// 16 tokens' K scales (lanes 0..31) and V scales (lanes 32..63).
+// K half-step of an FP8 step: 4 blocks of 1 KB, block j = tokens 4j..4j+3
+// read contiguously, chunk c (16 bytes) of token t at position c ^ (t & 3);
+// plus one 256-byte block holding the 16 tokens' K scales (lanes 0..31) and
+// V scales (lanes 32..63).
 __device__ __forceinline__ void dma_k8(const uint8_t* kb, const _Float16* ksb, const _Float16* vsb,
                                        char* stage, int lane) {
-  const uint8_t* src = kb + (lane & 15) * kHeadDim + 16 * (lane >> 4);
 #pragma unroll
-  for (int bk = 0; bk < 4; ++bk)
-    __builtin_amdgcn_global_load_lds(SV_GP(src + 64 * bk), SV_LP(stage + bk * 1024), 16, 0, 0);
+  for (int j = 0; j < 4; ++j) {
+    const int t = 4 * j + (lane >> 4);
+    const int c = (lane & 15) ^ (t & 3);
+    __builtin_amdgcn_global_load_lds(SV_GP(kb + t * kHeadDim + 16 * c), SV_LP(stage + j * 1024), 16, 0, 0);
+  }
   const _Float16* ssrc = lane < 32 ? ksb + 2 * lane : vsb + 2 * (lane - 32);
   __builtin_amdgcn_global_load_lds(SV_GP(ssrc), SV_LP(stage + 8192), 4, 0, 0);
 }
-// V half-step of an FP8 step: 16 blocks of 256 B, block 4e+bb lane l = bytes
-// 64bb + 4*(l%16) .. +4 of token 4*(l/16)+e.
+// V half-step of an FP8 step: the 4 KB of 16 tokens copied as is.
 __device__ __forceinline__ void dma_v8(const uint8_t* vb, char* stage, int lane) {
-  const uint8_t* src = vb + (4 * (lane >> 4)) * kHeadDim + 4 * (lane & 15);
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-      __builtin_amdgcn_global_load_lds(SV_GP(src + e * kHeadDim + 64 * bb),
-                                       SV_LP(stage + 4096 + (4 * e + bb) * 256), 4, 0, 0);
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_global_load_lds(SV_GP(vb + (j * kWave + lane) * 16), SV_LP(stage + 4096 + j * 1024), 16,
+                                     0, 0);
 }
+// Per-lane offsets: K block bk (bytes 64bk + 16*(l/16) of token l%16) at
+// k8_lane_off + 64*bk; V dword 4e+bb (bytes 64bb + 4*(l%16) of token
+// 4*(l/16)+e) at v8_lane_off + 64*(4e+bb).
+__device__ __forceinline__ uint32_t k8_lane_off(int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  return t * 256 + 16 * (g ^ (t & 3));
+}
+__device__ __forceinline__ uint32_t v8_lane_off(int lane) { return (lane >> 4) * 1024 + (lane & 15) * 4; }
 
 template <int VMCNT>
 __device__ __forceinline__ void ring_read_k8(KFrag8& f, uint32_t addr_lane, uint32_t addr_scale) {
   asm volatile(
       "s_waitcnt vmcnt(%10)\n\t"
       "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %1, %8 offset:64\n\t"
+      "ds_read_b128 %2, %8 offset:128\n\t"
+      "ds_read_b128 %3, %8 offset:192\n\t"
       "ds_read_b128 %4, %9\n\t"
       "ds_read_b128 %5, %9 offset:16\n\t"
       "ds_read_b128 %6, %9 offset:128\n\t"
       "ds_read_b128 %7, %9 offset:144\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(f.k[0]), "=v"(f.k[1]), "=v"(f.k[2]), "=v"(f.k[3]), "=v"(f.sk[0]), "=v"(f.sk[1]),
-        "=v"(f.sv[0]), "=v"(f.sv[1])
+      : "=&v"(f.k[0]), "=&v"(f.k[1]), "=&v"(f.k[2]), "=&v"(f.k[3]), "=&v"(f.sk[0]), "=&v"(f.sk[1]),
+        "=&v"(f.sv[0]), "=&v"(f.sv[1])
       : "v"(addr_lane), "v"(addr_scale), "n"(VMCNT)
       : "memory");
 }
@@ -449,25 +472,25 @@ __device__ __forceinline__ void ring_read_v8(VFrag8& f, uint32_t addr) {
   asm volatile(
       "s_waitcnt vmcnt(%17)\n\t"
       "ds_read_b32 %0, %16\n\t"
-      "ds_read_b32 %1, %16 offset:256\n\t"
-      "ds_read_b32 %2, %16 offset:512\n\t"
-      "ds_read_b32 %3, %16 offset:768\n\t"
-      "ds_read_b32 %4, %16 offset:1024\n\t"
-      "ds_read_b32 %5, %16 offset:1280\n\t"
-      "ds_read_b32 %6, %16 offset:1536\n\t"
-      "ds_read_b32 %7, %16 offset:1792\n\t"
-      "ds_read_b32 %8, %16 offset:2048\n\t"
-      "ds_read_b32 %9, %16 offset:2304\n\t"
-      "ds_read_b32 %10, %16 offset:2560\n\t"
-      "ds_read_b32 %11, %16 offset:2816\n\t"
-      "ds_read_b32 %12, %16 offset:3072\n\t"
-      "ds_read_b32 %13, %16 offset:3328\n\t"
-      "ds_read_b32 %14, %16 offset:3584\n\t"
-      "ds_read_b32 %15, %16 offset:3840\n\t"
+      "ds_read_b32 %1, %16 offset:64\n\t"
+      "ds_read_b32 %2, %16 offset:128\n\t"
+      "ds_read_b32 %3, %16 offset:192\n\t"
+      "ds_read_b32 %4, %16 offset:256\n\t"
+      "ds_read_b32 %5, %16 offset:320\n\t"
+      "ds_read_b32 %6, %16 offset:384\n\t"
+      "ds_read_b32 %7, %16 offset:448\n\t"
+      "ds_read_b32 %8, %16 offset:512\n\t"
+      "ds_read_b32 %9, %16 offset:576\n\t"
+      "ds_read_b32 %10, %16 offset:640\n\t"
+      "ds_read_b32 %11, %16 offset:704\n\t"
+      "ds_read_b32 %12, %16 offset:768\n\t"
+      "ds_read_b32 %13, %16 offset:832\n\t"
+      "ds_read_b32 %14, %16 offset:896\n\t"
+      "ds_read_b32 %15, %16 offset:960\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(f.v[0]), "=v"(f.v[1]), "=v"(f.v[2]), "=v"(f.v[3]), "=v"(f.v[4]), "=v"(f.v[5]),
-        "=v"(f.v[6]), "=v"(f.v[7]), "=v"(f.v[8]), "=v"(f.v[9]), "=v"(f.v[10]), "=v"(f.v[11]),
-        "=v"(f.v[12]), "=v"(f.v[13]), "=v"(f.v[14]), "=v"(f.v[15])
+      : "=&v"(f.v[0]), "=&v"(f.v[1]), "=&v"(f.v[2]), "=&v"(f.v[3]), "=&v"(f.v[4]), "=&v"(f.v[5]),
+        "=&v"(f.v[6]), "=&v"(f.v[7]), "=&v"(f.v[8]), "=&v"(f.v[9]), "=&v"(f.v[10]), "=&v"(f.v[11]),
+        "=&v"(f.v[12]), "=&v"(f.v[13]), "=&v"(f.v[14]), "=&v"(f.v[15])
       : "v"(addr), "n"(VMCNT)
       : "memory");
 }
@@ -560,7 +583,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   if constexpr (FP8) {
     // ---- FP8: each wave owns its token steps and a private 2-stage ring ----
     // (same schedule as the fp16 ring below; half-steps are K bytes + both
-    // scale sets (5 operations) and V bytes (16 operations))
+    // scale sets (5 operations) and V bytes (4 operations): 13 newer
+    // operations may be outstanding before a K read, 14 before a V read)
     char* ring = reinterpret_cast<char*>(bigsm) + wave * 2 * kStage8;
     const uint8_t* kpool8 = static_cast<const uint8_t*>(a.k_pages);
     const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
@@ -601,12 +625,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         const int kn = min(kk + 2, nb - 1);
         const uint32_t sbase = ring_lds + st * kStage8;
         KFrag8 kf;
-        ring_read_k8<37>(kf, sbase + lane * 16, sbase + 8192 + 32 * (lane >> 4));
+        ring_read_k8<13>(kf, sbase + k8_lane_off(lane), sbase + 8192 + 32 * (lane >> 4));
         issue_k(kn, st);
         float pr[RB][4];
         step_scores8<RB>(kf, qf, ws, pr, lane, t0, L, kv, growbase, R, G, a.scale_log2);
         VFrag8 vf;
-        ring_read_v8<26>(vf, sbase + 4096 + lane * 4);
+        ring_read_v8<14>(vf, sbase + 4096 + v8_lane_off(lane));
         issue_v(kn, st);
         step_pv8<RB>(vf, kf, pr, ws, lane, t0, kv);
       }
@@ -642,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       // exactly three newer half-steps (24 operations) may be outstanding.
       // Indices past the batch are clamped to its last step (a duplicate
       // request that hits in cache) to keep that count exact.
-      const uint32_t ring_lds = lds_addr(ring) + lane * 16;
+      const uint32_t ring_lds = lds_addr(ring);
       dma_k<0, 8>(step_base(0, kpool), ring, lane);
       dma_v<0, 8>(step_base(0, vpool), ring + 8192, lane);
       dma_k<0, 8>(step_base(min(1, nb - 1), kpool), ring + kRingStage, lane);
@@ -652,12 +676,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         const int t0 = step_t0(kk);
         const int kn = min(kk + 2, nb - 1);
         KFrag kf;
-        ring_read8<24, false>(kf.k, ring_lds + st);
+        ring_read8<24, false, 64>(kf.k, ring_lds + st + k_lane_off(lane));
         dma_k<0, 8>(step_base(kn, kpool), ring + st, lane);
         half4_t pb[RB];
         step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, growbase, R, G, a.scale_log2);
         VFrag vf;
-        ring_read8<24, false>(vf.v, ring_lds + st + 8192);
+        ring_read8<24, false, 256>(vf.v, ring_lds + st + 8192 + v_lane_off(lane));
         dma_v<0, 8>(step_base(kn, vpool), ring + st + 8192, lane);
         step_pv<RB>(vf, pb, ws, lane, t0, kv);
       }
@@ -673,7 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     // repeats its last one without computing) so every barrier is reached.
     constexpr int kStages = 3;
     char* pring = reinterpret_cast<char*>(bigsm) + ts * kStages * kRingStage;
-    const uint32_t pring_lds = lds_addr(pring) + lane * 16;
+    const uint32_t pring_lds = lds_addr(pring);
     const int all_steps = (n_steps + NTS - 1) / NTS;
     int pid0 = ptab[chunk_lo / P];  // a valid page for pairs with nothing to do
     if (pid0 < 0 || pid0 >= a.num_pages) {
@@ -723,13 +747,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         const int t0 = step_t0(kk);
         const bool work = kk < valid;
         KFrag kf;
-        ring_read8<12, true>(kf.k, pring_lds + st);
+        ring_read8<12, true, 64>(kf.k, pring_lds + st + k_lane_off(lane));
         if (rg == 0) dma_k<0, 4>(step_base(kk + 2, kpool), pring + st2, lane);
         else dma_k<4, 8>(step_base(kk + 2, kpool), pring + st2, lane);
         half4_t pb[RB];
         if (work) step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, growbase, R, G, a.scale_log2);
         VFrag vf;
-        ring_read8<12, true>(vf.v, pring_lds + st + 8192);
+        ring_read8<12, true, 256>(vf.v, pring_lds + st + 8192 + v_lane_off(lane));
         if (rg == 0) dma_v<0, 4>(step_base(kk + 2, vpool), pring + st2 + 8192, lane);
         else dma_v<4, 8>(step_base(kk + 2, vpool), pring + st2 + 8192, lane);
         if (work) step_pv<RB>(vf, pb, ws, lane, t0, kv);
