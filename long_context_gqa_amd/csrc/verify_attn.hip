@@ -495,17 +495,19 @@ __device__ __forceinline__ void ring_read_v8(VFrag8& f, uint32_t addr) {
       : "memory");
 }
 
-constexpr int kRingStage = 16384;               // K (8 KB) + V (8 KB) of one step
-constexpr int kRingPerWave = 2 * kRingStage;    // two stages per wave
+constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
+// A wave keeps one step in flight in its private ring (64 KB per CU over the
+// four waves): that saturates HBM for this access pattern, and on MI355X a
+// second step in flight per wave measured slower, not faster.
 
 template <int RB, int NRG, bool FP8>
 struct Smem {
   static constexpr int NTS = kWavesPerGroup / NRG;
   static constexpr int QBYTES = NRG * RB * 8 * kWave * 16;
   static constexpr int OBYTES = NRG * RB * 16 * kRowStride * 4;
-  // NRG 1: a private 2-stage ring per wave; NRG 2: a 3-stage ring per pair
-  static constexpr int RBYTES = FP8 ? kWavesPerGroup * 2 * kStage8
-                               : (NRG == 1 ? kWavesPerGroup * kRingPerWave : NTS * 3 * kRingStage);
+  // NRG 1: a private one-step ring per wave; NRG 2: a 3-stage ring per pair
+  static constexpr int RBYTES = FP8 ? kWavesPerGroup * kStage8
+                               : (NRG == 1 ? kWavesPerGroup * kRingStage : NTS * 3 * kRingStage);
   // Q fragments in their own array (so reading them never waits for the
   // ring's DMAs); the ring and, after the main loop, the combine buffer
   // share the second array.
@@ -581,11 +583,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const _Float16* vpool = static_cast<const _Float16*>(a.v_pages);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
   if constexpr (FP8) {
-    // ---- FP8: each wave owns its token steps and a private 2-stage ring ----
+    // ---- FP8: each wave owns its token steps and a private one-step ring ----
     // (same schedule as the fp16 ring below; half-steps are K bytes + both
-    // scale sets (5 operations) and V bytes (4 operations): 13 newer
-    // operations may be outstanding before a K read, 14 before a V read)
-    char* ring = reinterpret_cast<char*>(bigsm) + wave * 2 * kStage8;
+    // scale sets (5 operations) and V bytes (4 operations): the V half-step
+    // (4) is newer than a K read, the next K half-step (5) than a V read)
+    char* ring = reinterpret_cast<char*>(bigsm) + wave * kStage8;
     const uint8_t* kpool8 = static_cast<const uint8_t*>(a.k_pages);
     const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
     const uint32_t ring_lds = lds_addr(ring);
@@ -617,28 +619,25 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       };
       issue_k(0, 0);
       issue_v(0, 0);
-      issue_k(min(1, nb - 1), 1);
-      issue_v(min(1, nb - 1), 1);
       for (int kk = 0; kk < nb; ++kk) {
-        const int st = kk & 1;
         const int t0 = step_t0(kk);
-        const int kn = min(kk + 2, nb - 1);
-        const uint32_t sbase = ring_lds + st * kStage8;
+        const int kn = min(kk + 1, nb - 1);
+        const uint32_t sbase = ring_lds;
         KFrag8 kf;
-        ring_read_k8<13>(kf, sbase + k8_lane_off(lane), sbase + 8192 + 32 * (lane >> 4));
-        issue_k(kn, st);
+        ring_read_k8<4>(kf, sbase + k8_lane_off(lane), sbase + 8192 + 32 * (lane >> 4));
+        issue_k(kn, 0);
         float pr[RB][4];
         step_scores8<RB>(kf, qf, ws, pr, lane, t0, L, kv, growbase, R, G, a.scale_log2);
         VFrag8 vf;
-        ring_read_v8<14>(vf, sbase + 4096 + v8_lane_off(lane));
-        issue_v(kn, st);
+        ring_read_v8<5>(vf, sbase + 4096 + v8_lane_off(lane));
+        issue_v(kn, 0);
         step_pv8<RB>(vf, kf, pr, ws, lane, t0, kv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   } else if constexpr (NRG == 1) {
-    // ---- each wave owns its token steps and a private 2-stage LDS ring ----
-    char* ring = reinterpret_cast<char*>(bigsm) + wave * kRingPerWave;
+    // ---- each wave owns its token steps and a private one-step LDS ring ----
+    char* ring = reinterpret_cast<char*>(bigsm) + wave * kRingStage;
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       // page id of each of the next 64 steps of this wave, one per lane
       int pid = 0;
@@ -660,29 +659,26 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         const int pg = __builtin_amdgcn_readlane(pid, kk);
         return pool + (((size_t)pg * Hkv + g) * P + (t0 % P)) * kHeadDim;
       };
-      // Two steps in flight per wave in its ring (stage = step & 1), one in
-      // registers. Order of DMA issue: K(k+2) right after K(k) is read,
-      // V(k+2) right after V(k) is read, so before reading any half-step
-      // exactly three newer half-steps (24 operations) may be outstanding.
-      // Indices past the batch are clamped to its last step (a duplicate
-      // request that hits in cache) to keep that count exact.
+      // One step in flight per wave in its ring, one in registers. Order of
+      // DMA issue: K(k+1) right after K(k) is read, V(k+1) right after V(k)
+      // is read, so before reading a half-step exactly the other half-step
+      // (8 operations) is newer. The index past the batch is clamped to its
+      // last step (a duplicate request that hits in cache) to keep that
+      // count exact.
       const uint32_t ring_lds = lds_addr(ring);
       dma_k<0, 8>(step_base(0, kpool), ring, lane);
       dma_v<0, 8>(step_base(0, vpool), ring + 8192, lane);
-      dma_k<0, 8>(step_base(min(1, nb - 1), kpool), ring + kRingStage, lane);
-      dma_v<0, 8>(step_base(min(1, nb - 1), vpool), ring + kRingStage + 8192, lane);
       for (int kk = 0; kk < nb; ++kk) {
-        const int st = (kk & 1) * kRingStage;
         const int t0 = step_t0(kk);
-        const int kn = min(kk + 2, nb - 1);
+        const int kn = min(kk + 1, nb - 1);
         KFrag kf;
-        ring_read8<24, false, 64>(kf.k, ring_lds + st + k_lane_off(lane));
-        dma_k<0, 8>(step_base(kn, kpool), ring + st, lane);
+        ring_read8<8, false, 64>(kf.k, ring_lds + k_lane_off(lane));
+        dma_k<0, 8>(step_base(kn, kpool), ring, lane);
         half4_t pb[RB];
         step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, growbase, R, G, a.scale_log2);
         VFrag vf;
-        ring_read8<24, false, 256>(vf.v, ring_lds + st + 8192 + v_lane_off(lane));
-        dma_v<0, 8>(step_base(kn, vpool), ring + st + 8192, lane);
+        ring_read8<8, false, 256>(vf.v, ring_lds + 8192 + v_lane_off(lane));
+        dma_v<0, 8>(step_base(kn, vpool), ring + 8192, lane);
         step_pv<RB>(vf, pb, ws, lane, t0, kv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
