@@ -545,6 +545,51 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const bool direct = (n_chunks == 1);
   if (tid == 0) s_flag = 0;
 
+  const int n_steps = (chunk_hi > chunk_lo) ? (chunk_hi - chunk_lo + kStep - 1) / kStep : 0;
+  const int my_steps = n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0;
+  const int P = a.page_size, Hkv = a.num_kv_heads;
+  const _Float16* kpool = static_cast<const _Float16*>(a.k_pages);
+  const _Float16* vpool = static_cast<const _Float16*>(a.v_pages);
+  const uint8_t* kpool8 = static_cast<const uint8_t*>(a.k_pages);
+  const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
+  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+  // NRG 1: page id of each of the wave's steps bstart .. bstart+63, one per lane
+  auto page_ids = [&](int bstart) {
+    int pid = 0;
+    const int kl = bstart + lane;
+    if (kl < my_steps) {
+      const int t = chunk_lo + kStep * (ts + kl * NTS);
+      pid = ptab[t / P];
+      if (pid < 0 || pid >= a.num_pages) {
+        flag_bits |= 0x4;
+        pid = 0;
+      }
+    }
+    return pid;
+  };
+  // (page, KV head, slot) row of the first token of the wave's step bstart + kk
+  auto tok_row = [&](int pid, int bstart, int kk) {
+    const int pg = __builtin_amdgcn_readlane(pid, kk);
+    return ((size_t)pg * Hkv + g) * P + ((chunk_lo + kStep * (ts + (bstart + kk) * NTS)) % P);
+  };
+  char* const ring = reinterpret_cast<char*>(bigsm) + wave * (FP8 ? kStage8 : kRingStage);
+  // NRG 1: the first step's DMAs go out before Q is staged, so the two
+  // latencies overlap (Q lives in its own array; the ring is the wave's own)
+  int pid_first = 0;
+  if constexpr (NRG == 1) {
+    if (my_steps > 0) {
+      pid_first = page_ids(0);
+      const size_t tr = tok_row(pid_first, 0, 0);
+      if constexpr (FP8) {
+        dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring, lane);
+        dma_v8(vpool8 + tr * kHeadDim, ring, lane);
+      } else {
+        dma_k<0, 8>(kpool + tr * kHeadDim, ring, lane);
+        dma_v<0, 8>(vpool + tr * kHeadDim, ring + 8192, lane);
+      }
+    }
+  }
+
   // Q fragments of every row group into LDS, in MFMA B-operand order.
   u32x4* qlds = reinterpret_cast<u32x4*>(qsm);
   for (int idx = tid; idx < NRG * RB * 8 * kWave; idx += kThreads) {
@@ -576,49 +621,27 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const u32x4* qf = qlds + rg * RB * 8 * kWave;
   const int rowbase = rg * RB * 16;        // first row of this wave, local to the workgroup
   const int growbase = row0 + rowbase;     // the same row in the KV head's numbering
-  const int n_steps = (chunk_hi > chunk_lo) ? (chunk_hi - chunk_lo + kStep - 1) / kStep : 0;
-  const int my_steps = n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0;
-  const int P = a.page_size, Hkv = a.num_kv_heads;
-  const _Float16* kpool = static_cast<const _Float16*>(a.k_pages);
-  const _Float16* vpool = static_cast<const _Float16*>(a.v_pages);
-  const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
   if constexpr (FP8) {
     // ---- FP8: each wave owns its token steps and a private one-step ring ----
     // (same schedule as the fp16 ring below; half-steps are K bytes + both
     // scale sets (5 operations) and V bytes (4 operations): the V half-step
     // (4) is newer than a K read, the next K half-step (5) than a V read)
-    char* ring = reinterpret_cast<char*>(bigsm) + wave * kStage8;
-    const uint8_t* kpool8 = static_cast<const uint8_t*>(a.k_pages);
-    const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
     const uint32_t ring_lds = lds_addr(ring);
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
-      int pid = 0;
-      {
-        const int kl = bstart + lane;
-        if (kl < my_steps) {
-          const int t = chunk_lo + kStep * (ts + kl * NTS);
-          pid = ptab[t / P];
-          if (pid < 0 || pid >= a.num_pages) {
-            flag_bits |= 0x4;
-            pid = 0;
-          }
-        }
-      }
+      const int pid = bstart == 0 ? pid_first : page_ids(bstart);
       const int nb = min(kWave, my_steps - bstart);
       auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
-      auto tok_row = [&](int kk) {  // (page, KV head, slot) row index of the step's first token
-        const int pg = __builtin_amdgcn_readlane(pid, kk);
-        return ((size_t)pg * Hkv + g) * P + (step_t0(kk) % P);
-      };
       auto issue_k = [&](int kk, int stg) {
-        const size_t tr = tok_row(kk);
+        const size_t tr = tok_row(pid, bstart, kk);
         dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring + stg * kStage8, lane);
       };
       auto issue_v = [&](int kk, int stg) {
-        dma_v8(vpool8 + tok_row(kk) * kHeadDim, ring + stg * kStage8, lane);
+        dma_v8(vpool8 + tok_row(pid, bstart, kk) * kHeadDim, ring + stg * kStage8, lane);
       };
-      issue_k(0, 0);
-      issue_v(0, 0);
+      if (bstart > 0) {  // (the first batch's first step was issued before Q staging)
+        issue_k(0, 0);
+        issue_v(0, 0);
+      }
       for (int kk = 0; kk < nb; ++kk) {
         const int t0 = step_t0(kk);
         const int kn = min(kk + 1, nb - 1);
@@ -637,28 +660,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     }
   } else if constexpr (NRG == 1) {
     // ---- each wave owns its token steps and a private one-step LDS ring ----
-    char* ring = reinterpret_cast<char*>(bigsm) + wave * kRingStage;
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
-      // page id of each of the next 64 steps of this wave, one per lane
-      int pid = 0;
-      {
-        const int kl = bstart + lane;
-        if (kl < my_steps) {
-          const int t = chunk_lo + kStep * (ts + kl * NTS);
-          pid = ptab[t / P];
-          if (pid < 0 || pid >= a.num_pages) {
-            flag_bits |= 0x4;
-            pid = 0;
-          }
-        }
-      }
+      const int pid = bstart == 0 ? pid_first : page_ids(bstart);
       const int nb = min(kWave, my_steps - bstart);
       auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
-      auto step_base = [&](int kk, const _Float16* pool) {
-        const int t0 = step_t0(kk);
-        const int pg = __builtin_amdgcn_readlane(pid, kk);
-        return pool + (((size_t)pg * Hkv + g) * P + (t0 % P)) * kHeadDim;
-      };
+      auto step_base = [&](int kk, const _Float16* pool) { return pool + tok_row(pid, bstart, kk) * kHeadDim; };
       // One step in flight per wave in its ring, one in registers. Order of
       // DMA issue: K(k+1) right after K(k) is read, V(k+1) right after V(k)
       // is read, so before reading a half-step exactly the other half-step
@@ -666,8 +672,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       // last step (a duplicate request that hits in cache) to keep that
       // count exact.
       const uint32_t ring_lds = lds_addr(ring);
-      dma_k<0, 8>(step_base(0, kpool), ring, lane);
-      dma_v<0, 8>(step_base(0, vpool), ring + 8192, lane);
+      if (bstart > 0) {  // (the first batch's first step was issued before Q staging)
+        dma_k<0, 8>(step_base(0, kpool), ring, lane);
+        dma_v<0, 8>(step_base(0, vpool), ring + 8192, lane);
+      }
       for (int kk = 0; kk < nb; ++kk) {
         const int t0 = step_t0(kk);
         const int kn = min(kk + 1, nb - 1);
