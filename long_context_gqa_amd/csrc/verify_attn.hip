@@ -168,27 +168,21 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
 
 // ---- FP8 E4M3 steps -------------------------------------------------------
 //
-// E4M3 byte -> fp16 bit pattern whose value is the E4M3 value / 256: the sign
-// moves to bit 15 and exponent+mantissa (7 bits) land at bits 7..13, so the
-// fp16 exponent is the E4M3 exponent (bias 7 vs 15: a factor 2^-8) and
-// subnormals map to subnormals. Exact for every finite code; the factor 256
-// is folded into the per-block scales. Input: the two bytes placed at bits
-// 8..15 and 24..31 of t.
-__device__ __forceinline__ uint32_t e4m3_pair_to_f16(uint32_t t) {
-  return (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
+// E4M3 bytes become fp16 with the packed hardware conversion at scale 1.0:
+// every finite E4M3 value is an fp16 value (subnormals included), so the
+// conversion is exact; the per-block scales are applied outside the MFMAs in
+// fp32. Lanes see the pair (byte 0, byte 1) with word_sel false and (byte 2,
+// byte 3) with word_sel true, low byte in the low half.
+__device__ __forceinline__ uint32_t e4m3x2_lo(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
 }
-// bytes 0,1 and bytes 2,3 of w as two fp16 pairs (value / 256)
-__device__ __forceinline__ uint32_t e4m3_lo2(uint32_t w) {
-  return e4m3_pair_to_f16(((w << 8) & 0x0000FF00u) | ((w << 16) & 0xFF000000u));
+__device__ __forceinline__ uint32_t e4m3x2_hi(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
-__device__ __forceinline__ uint32_t e4m3_hi2(uint32_t w) {
-  return e4m3_pair_to_f16(((w >> 8) & 0x0000FF00u) | (w & 0xFF000000u));
-}
-// byte c of w0 and byte c of w1 as one fp16 pair (value / 256)
-__device__ __forceinline__ uint32_t e4m3_gather2(uint32_t w0, uint32_t w1, int c) {
-  const uint32_t b0 = (w0 >> (8 * c)) & 0xFFu, b1 = (w1 >> (8 * c)) & 0xFFu;
-  return e4m3_pair_to_f16((b0 << 8) | (b1 << 24));
-}
+// Interleave two words bytewise: {a.0, b.0, a.1, b.1} and {a.2, b.2, a.3, b.3}
+// (v_perm: selectors 0-3 take the second operand's bytes, 4-7 the first's).
+__device__ __forceinline__ uint32_t zip_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05010400u); }
+__device__ __forceinline__ uint32_t zip_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07030602u); }
 
 // One FP8 step held by a wave.
 //   k[b]  : token lane%16, bytes 64b + 16*(lane/16) .. +16 (the 64-channel scale
@@ -211,7 +205,7 @@ __device__ __forceinline__ float half_at(const u32x4 (&h)[2], int idx) {
 }
 
 // Scores of one FP8 step: per 64-channel block, two MFMAs on the converted
-// K, then S = sum_b (256 * scale_b) * partial_b.
+// K, then S = sum_b scale_b * partial_b.
 template <int RB>
 __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __restrict__ qf,
                                              WaveState<RB>& ws, float (&p)[RB][4], int lane, int t0,
@@ -220,16 +214,16 @@ __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __re
   u32x4 kc[8];
 #pragma unroll
   for (int bk = 0; bk < 4; ++bk) {
-    kc[2 * bk] = u32x4{e4m3_lo2(kf.k[bk][0]), e4m3_hi2(kf.k[bk][0]), e4m3_lo2(kf.k[bk][1]),
-                       e4m3_hi2(kf.k[bk][1])};
-    kc[2 * bk + 1] = u32x4{e4m3_lo2(kf.k[bk][2]), e4m3_hi2(kf.k[bk][2]), e4m3_lo2(kf.k[bk][3]),
-                           e4m3_hi2(kf.k[bk][3])};
+    kc[2 * bk] = u32x4{e4m3x2_lo(kf.k[bk][0]), e4m3x2_hi(kf.k[bk][0]), e4m3x2_lo(kf.k[bk][1]),
+                       e4m3x2_hi(kf.k[bk][1])};
+    kc[2 * bk + 1] = u32x4{e4m3x2_lo(kf.k[bk][2]), e4m3x2_hi(kf.k[bk][2]), e4m3x2_lo(kf.k[bk][3]),
+                           e4m3x2_hi(kf.k[bk][3])};
   }
   float fk[4][4];  // [token i][block]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * (256.f * scale_log2);
+    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * scale_log2;
   float x[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -253,24 +247,28 @@ __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __re
 }
 
 // O^T += V^T . P^T for one FP8 step: MFMA block j = 4*bb + c holds channels
-// 64*bb + 4*(lane%16) + c, all inside scale block bb, so the V scale (times
-// 256) is folded into P^T once per block group and V is used exactly.
+// 64*bb + 4*(lane%16) + c, all inside scale block bb, so the V scale is folded
+// into P^T once per block group and V is used exactly.
 template <int RB>
-__device__ __forceinline__ void step_pv8(const VFrag8& vf, const KFrag8& kf, const float (&p)[RB][4],
+__device__ __forceinline__ void step_pv8(VFrag8& vf, const KFrag8& kf, const float (&p)[RB][4],
                                          WaveState<RB>& ws, int lane, int t0, int kv) {
   const int hi = lane >> 4;
   float fv[4][4];  // [token i][block]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) fv[i][bb] = half_at(kf.sv, 4 * i + bb) * 256.f;
-  // keys at or past kv_len: weight 0, and their (poison) scale must not enter
+    for (int bb = 0; bb < 4; ++bb) fv[i][bb] = half_at(kf.sv, 4 * i + bb);
+  // Keys at or past kv_len: weight 0; their (poison) scales must not enter
+  // and their bytes may decode to NaN (0 * NaN is NaN), so clear both.
   if (t0 + kStep > kv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (t0 + 4 * hi + i >= kv) {
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) fv[i][bb] = 0.f;
+        for (int bb = 0; bb < 4; ++bb) {
+          fv[i][bb] = 0.f;
+          vf.v[4 * i + bb] = 0u;
+        }
       }
   }
 #pragma unroll
@@ -280,10 +278,15 @@ __device__ __forceinline__ void step_pv8(const VFrag8& vf, const KFrag8& kf, con
     for (int rb = 0; rb < RB; ++rb)
       pb[rb] = half4_t{(_Float16)(p[rb][0] * fv[0][bb]), (_Float16)(p[rb][1] * fv[1][bb]),
                        (_Float16)(p[rb][2] * fv[2][bb]), (_Float16)(p[rb][3] * fv[3][bb])};
+    // tokens (0, 1) and (2, 3) of the lane's group, byte c of block bb, as
+    // fp16 pairs: A operand halves of channel 64*bb + 4*(lane%16) + c
+    const uint32_t z01l = zip_lo(vf.v[bb], vf.v[4 + bb]), z01h = zip_hi(vf.v[bb], vf.v[4 + bb]);
+    const uint32_t z23l = zip_lo(vf.v[8 + bb], vf.v[12 + bb]), z23h = zip_hi(vf.v[8 + bb], vf.v[12 + bb]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t a0 = e4m3_gather2(vf.v[0 * 4 + bb], vf.v[1 * 4 + bb], c);
-      const uint32_t a1 = e4m3_gather2(vf.v[2 * 4 + bb], vf.v[3 * 4 + bb], c);
+      const uint32_t w01 = c < 2 ? z01l : z01h, w23 = c < 2 ? z23l : z23h;
+      const uint32_t a0 = (c & 1) ? e4m3x2_hi(w01) : e4m3x2_lo(w01);
+      const uint32_t a1 = (c & 1) ? e4m3x2_hi(w23) : e4m3x2_lo(w23);
       const int j = 4 * bb + c;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) ws.o[rb][j] = mfma_16x16x16(a0, a1, pb[rb], ws.o[rb][j]);
