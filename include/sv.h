@@ -62,7 +62,7 @@ typedef struct {
   int32_t batch;             /* B >= 1 requests */
   int32_t q_len;             /* verify rows per request, 1..16 */
   int32_t num_q_heads;       /* Hq; query head h uses KV head h / (Hq/Hkv) */
-  int32_t num_kv_heads;      /* Hkv, divides Hq; q_len * Hq/Hkv <= 96 (<= 48 for FP8 KV) */
+  int32_t num_kv_heads;      /* Hkv, divides Hq; q_len * Hq/Hkv <= 96 */
   int32_t head_dim;          /* D, must be 256 */
   int32_t page_size;         /* P tokens per page: a multiple of 16, at most 4096 */
   int32_t num_pages;         /* pages in the pool (bounds page ids) */

@@ -53,7 +53,7 @@ int cu_count() {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Plan {
-  int rb, nrg;         // row blocks of 16 per wave, row groups per workgroup
+  int rb, row_blocks;  // row blocks of 16 per workgroup; workgroups per (chunk, KV head, request)
   int splits, chunk;   // key chunks and their length in tokens
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
@@ -102,14 +102,15 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   const int R = p->q_len * G;
   const int rbt = (R + 15) / 16;
   if (rbt <= 3) {
-    pl->nrg = 1;
+    pl->row_blocks = 1;
     pl->rb = rbt;
   } else {
-    pl->nrg = 2;
-    pl->rb = 3;
+    // more than 48 rows: two workgroups of up to 48 rows read the same keys
+    pl->row_blocks = 2;
+    pl->rb = (rbt + 1) / 2;
   }
   const long long maxkv = p->max_kv_len;
-  const long long rgs = 1;  // workgroups per (chunk, KV head, request)
+  const long long rgs = pl->row_blocks;  // workgroups per (chunk, KV head, request)
   long long S;
   if (p->num_splits > 0) {
     S = p->num_splits;
@@ -134,6 +135,8 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
   S = (maxkv + chunk - 1) / chunk;
+  if (S * p->num_kv_heads * p->batch * 2 * rgs > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "too many workgroups (%lld splits)", S);
   pl->splits = (int)S;
   pl->chunk = (int)chunk;
   if (S > 1) {
@@ -179,8 +182,6 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
   if (p->kv_dtype == SV_KV_FP8_E4M3) {
     if (!k_scales || !v_scales)
       return fail(SV_ERR_INVALID_ARGUMENT, "FP8 KV needs k_scales and v_scales");
-    if (pl.nrg != 1)
-      return fail(SV_ERR_UNSUPPORTED, "FP8 KV supports q_len * (num_q_heads/num_kv_heads) <= 48");
   } else if (k_scales || v_scales) {
     return fail(SV_ERR_INVALID_ARGUMENT, "k_scales/v_scales must be NULL for fp16 KV");
   }
@@ -218,7 +219,9 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
   a.chunk = pl.chunk;
   a.num_splits = pl.splits;
   a.scale_log2 = p->sm_scale * 1.44269504088896340736f;
-  sv::launch_verify_attention(a, pl.rb, pl.nrg, p->kv_dtype == SV_KV_FP8_E4M3, s);
+  a.row_blocks = pl.row_blocks;
+  a.units = pl.splits * p->num_kv_heads * p->batch;
+  sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
   if (pl.splits > 1) {

@@ -34,6 +34,8 @@ struct AttnArgs {
   int32_t* flags;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group, page_size;
   int32_t num_pages, max_pages, max_kv_len, chunk, num_splits;
+  int32_t row_blocks;  // workgroups per (chunk, KV head, request): 1, or 2 for > 48 rows
+  int32_t units;       // num_splits * num_kv_heads * batch
   float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -60,7 +62,7 @@ __device__ inline int clamp_kv_len(int raw, int max_kv_len, int max_pages, int p
   return v;
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, int nrg, bool fp8, hipStream_t s);
+void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s);
 void launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace sv

@@ -21,12 +21,14 @@
 // A and B slots is relied on, plus the accumulator layout
 // (lane l holds rows 4*(l/16)+i, column l%16).
 //
-// The chunk's 16-token steps are dealt round-robin to the waves of the
-// workgroup (4 waves; 2 when the rows need two row groups). Each wave keeps
-// one step of K/V in flight while it computes the previous one. At the end
-// the waves' (m, l, O) are combined through LDS and the workgroup writes
-// either the final fp16 rows (request fits one chunk) or an fp32 partial
-// (o normalised, lse) for the merge kernel.
+// The chunk's 16-token steps are dealt round-robin to the 4 waves of the
+// workgroup. Each wave keeps one step of K/V in flight while it computes the
+// previous one. At the end the waves' (m, l, O) are combined through LDS and
+// the workgroup writes either the final fp16 rows (request fits one chunk)
+// or an fp32 partial (o normalised, lse) for the merge kernel. A workgroup
+// holds at most 48 rows; a KV head with more (up to 96) is covered by two
+// workgroups that read the same keys, placed on the same XCD so that the
+// second read is mostly served by its L2.
 #include "sv_common.h"
 
 namespace sv {
@@ -503,37 +505,46 @@ constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
 // four waves): that saturates HBM for this access pattern, and on MI355X a
 // second step in flight per wave measured slower, not faster.
 
-template <int RB, int NRG, bool FP8>
+template <int RB, bool FP8>
 struct Smem {
-  static constexpr int NTS = kWavesPerGroup / NRG;
-  static constexpr int QBYTES = NRG * RB * 8 * kWave * 16;
-  static constexpr int OBYTES = NRG * RB * 16 * kRowStride * 4;
-  // NRG 1: a private one-step ring per wave; NRG 2: a 3-stage ring per pair
-  static constexpr int RBYTES = FP8 ? kWavesPerGroup * kStage8
-                               : (NRG == 1 ? kWavesPerGroup * kRingStage : NTS * 3 * kRingStage);
+  static constexpr int QBYTES = RB * 8 * kWave * 16;
+  static constexpr int OBYTES = RB * 16 * kRowStride * 4;
+  // a private one-step ring per wave
+  static constexpr int RBYTES = kWavesPerGroup * (FP8 ? kStage8 : kRingStage);
   // Q fragments in their own array (so reading them never waits for the
   // ring's DMAs); the ring and, after the main loop, the combine buffer
   // share the second array.
   static constexpr int BIG = RBYTES > OBYTES ? RBYTES : OBYTES;
 };
 
-template <int RB, int NRG, bool FP8>
+template <int RB, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
-  static_assert(!FP8 || NRG == 1, "FP8 KV is built for up to 48 rows per KV head");
-  using SM = Smem<RB, NRG, FP8>;
-  constexpr int NTS = SM::NTS;   // waves sharing one row group
+  using SM = Smem<RB, FP8>;
+  constexpr int NTS = kWavesPerGroup;  // waves that split the chunk's steps
   __shared__ __attribute__((aligned(1024))) unsigned char qsm[SM::QBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char bigsm[SM::BIG];
-  __shared__ float s_m[NTS][NRG * RB * 16];
-  __shared__ float s_l[NTS][NRG * RB * 16];
+  __shared__ float s_m[NTS][RB * 16];
+  __shared__ float s_l[NTS][RB * 16];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  const int rg = wave % NRG, ts = wave / NRG;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int split = blockIdx.x;
-  const int row0 = 0;  // first row (of the KV head's q_len*G) of this workgroup
+  const int ts = wave;
+  // Workgroup -> (key chunk, KV head, request, row block). With two row
+  // blocks the pair that shares a (chunk, KV head, request) gets ids 8 apart
+  // in the same group of 16, i.e. the same XCD at about the same time (ids
+  // go round-robin over the 8 XCDs), so the second reader of each K/V byte
+  // mostly finds it in that XCD's L2.
+  int unit = blockIdx.x, rblk = 0;
+  if (a.row_blocks == 2) {
+    const int r = blockIdx.x >> 3;
+    rblk = r & 1;
+    unit = ((r >> 1) << 3) | (blockIdx.x & 7);
+    if (unit >= a.units) return;
+  }
+  const int split = unit % a.num_splits;
+  const int g = (unit / a.num_splits) % a.num_kv_heads, b = unit / a.num_splits / a.num_kv_heads;
+  const int row0 = rblk * RB * 16;  // first row (of the KV head's q_len*G) of this workgroup
   const int q_len = a.q_len, G = a.group, R = q_len * G, Hq = a.num_q_heads;
 
   int flag_bits = 0;
@@ -556,7 +567,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const uint8_t* kpool8 = static_cast<const uint8_t*>(a.k_pages);
   const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
-  // NRG 1: page id of each of the wave's steps bstart .. bstart+63, one per lane
+  // page id of each of the wave's steps bstart .. bstart+63, one per lane
   auto page_ids = [&](int bstart) {
     int pid = 0;
     const int kl = bstart + lane;
@@ -576,29 +587,27 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     return ((size_t)pg * Hkv + g) * P + ((chunk_lo + kStep * (ts + (bstart + kk) * NTS)) % P);
   };
   char* const ring = reinterpret_cast<char*>(bigsm) + wave * (FP8 ? kStage8 : kRingStage);
-  // NRG 1: the first step's DMAs go out before Q is staged, so the two
-  // latencies overlap (Q lives in its own array; the ring is the wave's own)
+  // The first step's DMAs go out before Q is staged, so the two latencies
+  // overlap (Q lives in its own array; the ring is the wave's own).
   int pid_first = 0;
-  if constexpr (NRG == 1) {
-    if (my_steps > 0) {
-      pid_first = page_ids(0);
-      const size_t tr = tok_row(pid_first, 0, 0);
-      if constexpr (FP8) {
-        dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring, lane);
-        dma_v8(vpool8 + tr * kHeadDim, ring, lane);
-      } else {
-        dma_k<0, 8>(kpool + tr * kHeadDim, ring, lane);
-        dma_v<0, 8>(vpool + tr * kHeadDim, ring + 8192, lane);
-      }
+  if (my_steps > 0) {
+    pid_first = page_ids(0);
+    const size_t tr = tok_row(pid_first, 0, 0);
+    if constexpr (FP8) {
+      dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring, lane);
+      dma_v8(vpool8 + tr * kHeadDim, ring, lane);
+    } else {
+      dma_k<0, 8>(kpool + tr * kHeadDim, ring, lane);
+      dma_v<0, 8>(vpool + tr * kHeadDim, ring + 8192, lane);
     }
   }
 
-  // Q fragments of every row group into LDS, in MFMA B-operand order.
+  // Q fragments of the workgroup's rows into LDS, in MFMA B-operand order.
   u32x4* qlds = reinterpret_cast<u32x4*>(qsm);
-  for (int idx = tid; idx < NRG * RB * 8 * kWave; idx += kThreads) {
+  for (int idx = tid; idx < RB * 8 * kWave; idx += kThreads) {
     const int frag = idx / kWave, ln = idx % kWave;
-    const int rgi = frag / (RB * 8), rb = (frag / 8) % RB, s = frag % 8;
-    const int r = row0 + (rgi * RB + rb) * 16 + (ln & 15);
+    const int rb = frag / 8, s = frag % 8;
+    const int r = row0 + rb * 16 + (ln & 15);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < R) {
       const int i = r / G, j = r % G;
@@ -621,9 +630,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     for (int j = 0; j < 16; ++j) ws.o[rb][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const u32x4* qf = qlds + rg * RB * 8 * kWave;
-  const int rowbase = rg * RB * 16;        // first row of this wave, local to the workgroup
-  const int growbase = row0 + rowbase;     // the same row in the KV head's numbering
+  const u32x4* qf = qlds;
+  const int rowbase = 0;               // first row of the wave, local to the workgroup
+  const int growbase = row0 + rowbase;  // the same row in the KV head's numbering
   if constexpr (FP8) {
     // ---- FP8: each wave owns its token steps and a private one-step ring ----
     // (same schedule as the fp16 ring below; half-steps are K bytes + both
@@ -661,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-  } else if constexpr (NRG == 1) {
+  } else {
     // ---- each wave owns its token steps and a private one-step LDS ring ----
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const int pid = bstart == 0 ? pid_first : page_ids(bstart);
@@ -693,81 +702,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         step_pv<RB>(vf, pb, ws, lane, t0, kv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-  } else {
-    // ---- the two waves of a pair (same token steps, different rows) share
-    // a 3-stage ring: each issues half of every step's DMA blocks, and one
-    // workgroup barrier per half-step makes both halves visible. With three
-    // stages, the stage a DMA overwrites was last read one iteration ago, so
-    // the barrier before the current read also orders that reuse. All waves
-    // run the same number of iterations (the pair with fewer real steps
-    // repeats its last one without computing) so every barrier is reached.
-    constexpr int kStages = 3;
-    char* pring = reinterpret_cast<char*>(bigsm) + ts * kStages * kRingStage;
-    const uint32_t pring_lds = lds_addr(pring);
-    const int all_steps = (n_steps + NTS - 1) / NTS;
-    int pid0 = ptab[chunk_lo / P];  // a valid page for pairs with nothing to do
-    if (pid0 < 0 || pid0 >= a.num_pages) {
-      flag_bits |= 0x4;
-      pid0 = 0;
-    }
-    pid0 = __builtin_amdgcn_readfirstlane(pid0);
-    for (int bstart = 0; bstart < all_steps; bstart += kWave) {
-      int pid = 0;
-      {
-        const int kl = bstart + lane;
-        if (kl < my_steps) {
-          const int t = chunk_lo + kStep * (ts + kl * NTS);
-          pid = ptab[t / P];
-          if (pid < 0 || pid >= a.num_pages) {
-            flag_bits |= 0x4;
-            pid = 0;
-          }
-        }
-      }
-      const int nb = min(kWave, all_steps - bstart);
-      const int valid = max(0, min(nb, my_steps - bstart));  // steps this pair computes
-      auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
-      auto step_base = [&](int kk, const _Float16* pool) {
-        if (valid == 0) return pool + (((size_t)pid0 * Hkv + g) * P + (chunk_lo % P)) * kHeadDim;
-        const int kc = min(kk, valid - 1);
-        const int t0 = step_t0(kc);
-        const int pg = __builtin_amdgcn_readlane(pid, kc);
-        return pool + (((size_t)pg * Hkv + g) * P + (t0 % P)) * kHeadDim;
-      };
-      auto stage = [&](int kk) { return (kk % kStages) * kRingStage; };
-      // each wave issues 4 of the 8 blocks of every half-step: 12 newer
-      // operations may be outstanding before a read
-      if (rg == 0) {
-        dma_k<0, 4>(step_base(0, kpool), pring + stage(0), lane);
-        dma_v<0, 4>(step_base(0, vpool), pring + stage(0) + 8192, lane);
-        dma_k<0, 4>(step_base(1, kpool), pring + stage(1), lane);
-        dma_v<0, 4>(step_base(1, vpool), pring + stage(1) + 8192, lane);
-      } else {
-        dma_k<4, 8>(step_base(0, kpool), pring + stage(0), lane);
-        dma_v<4, 8>(step_base(0, vpool), pring + stage(0) + 8192, lane);
-        dma_k<4, 8>(step_base(1, kpool), pring + stage(1), lane);
-        dma_v<4, 8>(step_base(1, vpool), pring + stage(1) + 8192, lane);
-      }
-      for (int kk = 0; kk < nb; ++kk) {
-        const int st = stage(kk), st2 = stage(kk + 2);
-        const int t0 = step_t0(kk);
-        const bool work = kk < valid;
-        KFrag kf;
-        ring_read8<12, true, 64>(kf.k, pring_lds + st + k_lane_off(lane));
-        if (rg == 0) dma_k<0, 4>(step_base(kk + 2, kpool), pring + st2, lane);
-        else dma_k<4, 8>(step_base(kk + 2, kpool), pring + st2, lane);
-        half4_t pb[RB];
-        if (work) step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, growbase, R, G, a.scale_log2);
-        VFrag vf;
-        ring_read8<12, true, 256>(vf.v, pring_lds + st + 8192 + v_lane_off(lane));
-        if (rg == 0) dma_v<0, 4>(step_base(kk + 2, vpool), pring + st2 + 8192, lane);
-        else dma_v<4, 8>(step_base(kk + 2, vpool), pring + st2 + 8192, lane);
-        if (work) step_pv<RB>(vf, pb, ws, lane, t0, kv);
-      }
-      // drain, and keep the next batch's first DMAs off stages a slower wave
-      // may still be reading
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
   }
 
@@ -868,7 +802,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     }
   }
   // rows out: 32 threads per row, 8 channels per thread
-  const int rows_here = min(R - row0, NRG * RB * 16);
+  const int rows_here = min(R - row0, RB * 16);
   for (int lr = tid / 32; lr < rows_here; lr += kThreads / 32) {
     const int r = row0 + lr;
     const int d0 = (tid % 32) * 8;
@@ -890,19 +824,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   if (tid == 0 && s_flag && a.flags) atomicOr(a.flags, s_flag);
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, int nrg, bool fp8, hipStream_t s) {
-  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
-  dim3 block(kThreads);
+void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s) {
+  // one workgroup per unit; with two row blocks, 16 ids per 8 units
+  const int n = a.row_blocks == 2 ? 2 * ((a.units + 7) / 8 * 8) : a.units;
+  dim3 grid(n), block(kThreads);
   if (fp8) {
-    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, 1, true>), grid, block, 0, s, a);
-    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, 1, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((verify_attn_kernel<3, 1, true>), grid, block, 0, s, a);
-  } else if (nrg == 1) {
-    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, 1, false>), grid, block, 0, s, a);
-    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, 1, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((verify_attn_kernel<3, 1, false>), grid, block, 0, s, a);
+    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, true>), grid, block, 0, s, a);
+    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_attn_kernel<3, true>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((verify_attn_kernel<3, 2, false>), grid, block, 0, s, a);
+    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false>), grid, block, 0, s, a);
+    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_attn_kernel<3, false>), grid, block, 0, s, a);
   }
 }
 

@@ -213,9 +213,15 @@ def test_fp8_one_hot_probe_is_exact():
             assert np.array_equal(out[i, 6 * gq], want)
 
 
-def test_fp8_more_than_48_rows_is_rejected():
-    from long_context_gqa_amd import binding as B
-    x = case(1, 16, [100], 16, "unit", seed=1, kv_dtype="fp8_e4m3")
-    with pytest.raises(B.SvError) as e:
-        run_gpu(x)
-    assert e.value.status == B.SV_ERR_UNSUPPORTED
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3"])
+@pytest.mark.parametrize("Hq,q_len", [(16, 16), (20, 16), (24, 16), (24, 12)])
+def test_more_than_48_rows_two_row_blocks(kv_dtype, Hq, q_len):
+    # 64, 80, 96 and 72 rows per KV head: two workgroups of up to 48 rows
+    # read the same keys; ragged lengths, split and unsplit
+    x = case(3, q_len, [q_len + 5, 1000, 2333], 16, "unit", seed=Hq + q_len, kv_dtype=kv_dtype, Hq=Hq, Hkv=4)
+    ref, ref_lse = oracle(x)
+    for splits in (1, 0, 5):
+        say(f"{kv_dtype} Hq={Hq} q={q_len} rows={q_len * Hq // 4} splits={splits}")
+        out, lse, flags = run_gpu(x, num_splits=splits)
+        assert flags == 0
+        check(out, lse, ref, ref_lse, what=f"{q_len * Hq // 4} rows splits={splits}")
