@@ -35,7 +35,7 @@ struct AttnArgs {
   int32_t batch, q_len, num_q_heads, num_kv_heads, group, page_size;
   int32_t num_pages, max_pages, max_kv_len, chunk, num_splits;
   int32_t row_blocks;  // workgroups per (chunk, KV head, request): 1, or 2 for > 48 rows
-  int32_t units;       // num_splits * num_kv_heads * batch
+  int32_t units;       // num_splits * num_kv_heads * batch, numbered split-major
   float scale_log2;  // sm_scale * log2(e)
 };
 

@@ -542,8 +542,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     unit = ((r >> 1) << 3) | (blockIdx.x & 7);
     if (unit >= a.units) return;
   }
-  const int split = unit % a.num_splits;
-  const int g = (unit / a.num_splits) % a.num_kv_heads, b = unit / a.num_splits / a.num_kv_heads;
+  // Units are numbered split-major: every (KV head, request) of chunk 0,
+  // then chunk 1, ... Consecutive ids (which go to consecutive XCDs) then
+  // differ in head and request rather than in chunk, so ragged batches spread
+  // evenly over the XCDs, and the sparse late chunks of long requests are
+  // dispatched last.
+  const int hb = unit % (a.num_kv_heads * a.batch);
+  const int split = unit / (a.num_kv_heads * a.batch);
+  const int g = hb % a.num_kv_heads, b = hb / a.num_kv_heads;
   const int row0 = rblk * RB * 16;  // first row (of the KV head's q_len*G) of this workgroup
   const int q_len = a.q_len, G = a.group, R = q_len * G, Hq = a.num_q_heads;
 
