@@ -45,6 +45,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-splits", default=None,
                     help="comma-separated split counts: time the verify attention call at each")
+    ap.add_argument("--q-sweep", default=None,
+                    help="comma list of q_len: the same K/V (same bytes) verified with that many rows per request")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time the attention call after writing 1 GiB (evicting L2 and the Infinity Cache)")
+    ap.add_argument("--reference-copy-mib", type=int, default=0,
+                    help="time a device-to-device copy of this size as an attainable-bandwidth reference")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic", default=None,
@@ -173,6 +179,53 @@ def main():
                 f"{attn_bytes / (us * 1e-6) / 1e9:8.1f} GB/s")
             del c2
 
+    qsw = None
+    if args.q_sweep:
+        # fixed bytes: the same cache and lengths, q rows per request taken
+        # from the workload's first verify row of each request
+        qsw = {}
+        q4 = x.q.view(wl.batch, wl.q_len, wl.num_q_heads, wl.head_dim)
+        for qq in [int(v) for v in args.q_sweep.split(",")]:
+            qx = q4[:, :1].repeat(1, qq, 1, 1).reshape(wl.batch * qq, wl.num_q_heads, wl.head_dim).contiguous()
+            c2 = B.VerifyCall(qx, x.k_pages, x.v_pages, page_table, kv_lens, qq, x.max_kv_len,
+                              x.k_scales, x.v_scales, x.sm_scale, 0)
+            for _ in range(3):
+                c2.run(stream)
+            us = float(np.median(timed(lambda: c2.run(stream), n_part)))
+            qb = W.verify_algorithmic_bytes(x.kv_lens.tolist(), qq, wl.num_q_heads, wl.num_kv_heads,
+                                            wl.head_dim, wl.page_size, wl.kv_dtype)
+            qsw[str(qq)] = {"us": round(us, 2), "splits": c2.splits, "GBps": round(qb / (us * 1e-6) / 1e9, 1)}
+            log(f"[bench] q_len {qq:2d}: {us:8.2f} us  {qb / (us * 1e-6) / 1e9:8.1f} GB/s")
+            del c2, qx
+
+    cold = None
+    if args.cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_part)]
+        for i, (a, b) in enumerate(evs):
+            flush.fill_(i & 0xFF)
+            a.record(stream)
+            call.run(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        cus = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+        cold = {"us_median": round(float(np.median(cus)), 2),
+                "effective_GBps": round(attn_bytes / (np.median(cus) * 1e-6) / 1e9, 1),
+                "note": "1 GiB written before each call; warm figures above"}
+        del flush
+
+    ref_copy = None
+    if args.reference_copy_mib:
+        n = args.reference_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        us = float(np.median(timed(lambda: dst.copy_(src), 20)))
+        ref_copy = {"bytes_moved": 2 * n, "us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1),
+                    "note": "device copy (read + write) as an attainable-bandwidth reference"}
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wl)
@@ -226,6 +279,9 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
         "split_sweep": sweep,
+        "q_sweep": qsw,
+        "verify_attention_cold": cold,
+        "reference_copy": ref_copy,
     }
     print(json.dumps(res), flush=True)
 
@@ -282,7 +338,8 @@ def cpu_baseline(x, wl):
         "cores": threads,
         "kind": "oracle",
         "sample": f"float64 oracle, request 0 KV head 0: {wl.q_len}x{G} rows over {n} keys "
-                  f"({sample_bytes} algorithmic bytes) in {dt:.2f} s; host has {os.cpu_count()} CPUs",
+                  f"({sample_bytes} algorithmic bytes) in {dt:.2f} s; host has {os.cpu_count()} CPUs, "
+                  f"{len(os.sched_getaffinity(0))} usable by this process",
         "seconds": round(dt, 2),
     }
 
