@@ -6,8 +6,13 @@ from the pages' definitions:
   * ``attention.verify_attention`` — causal grouped-query attention of a
     verify block over a paged KV cache (fp16 or FP8 E4M3 + fp16 scales);
   * ``attention.merge_partials``   — combining split-KV partials (o, lse);
+  * ``attention.verify_attention_ragged`` — the same with a different block
+    width per request (rows packed request by request);
   * ``accept.greedy_accept``       — argmax per row, longest matching draft
-    prefix, bonus token, new cache length;
+    prefix, bonus token, new cache length (``greedy_accept_ragged``: per-request
+    widths);
+  * ``block.prepare_block`` / ``block.append_kv`` — a block's packed rows,
+    positions and cache slots, and writing its K/V into the reserved slots;
   * ``fp8.e4m3_decode``            — the OCP E4M3 value of each byte;
   * ``brute``                      — pure-Python loop versions for tiny inputs.
 

@@ -55,3 +55,38 @@ def greedy_accept(logits, draft_ids, q_len, kv_lens=None):
     am = row_argmax(logits)
     acc, bonus, new_lens = accept_from_argmax(am, draft_ids, q_len, kv_lens)
     return acc, bonus, am, new_lens
+
+
+def greedy_accept_ragged(logits, block_ids, q_lens, q_start, kv_lens=None):
+    """Greedy acceptance of blocks whose width differs per request.
+
+    Request b's rows are q_start[b] .. q_start[b] + q_b - 1 of logits and of
+    block_ids ([t0, d1, ..., d_{q_b-1}], packed as the block-preparation step
+    lays them out), so the draft checked against row j is the block id one
+    row later. Same rule as ``accept_from_argmax``: A is the longest prefix of
+    drafts equal to the target's argmax of the previous row, the bonus is row
+    A's argmax, and the cache keeps kv_len - q_b + 1 + A positions.
+
+    Returns (accept_len [B], bonus [B], argmax [rows], new_kv_lens or None).
+    """
+    if hasattr(logits, "detach"):
+        logits = logits.detach().cpu().numpy()
+    am = np.argmax(np.asarray(logits), axis=-1).astype(np.int64)
+    ids = np.asarray(block_ids.detach().cpu().numpy() if hasattr(block_ids, "detach") else block_ids,
+                     dtype=np.int64)
+    qn = np.asarray(q_lens, dtype=np.int64)
+    qs = np.asarray(q_start, dtype=np.int64)
+    B = len(qn)
+    acc = np.zeros(B, dtype=np.int64)
+    bonus = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        r0, qb = int(qs[b]), int(qn[b])
+        a = 0
+        while a < qb - 1 and ids[r0 + a + 1] == am[r0 + a]:
+            a += 1
+        acc[b] = a
+        bonus[b] = am[r0 + a]
+    new_lens = None
+    if kv_lens is not None:
+        new_lens = np.asarray(kv_lens, dtype=np.int64) - qn + 1 + acc
+    return acc, bonus, am, new_lens

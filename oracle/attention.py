@@ -177,3 +177,47 @@ def merge_partials(part_o, part_lse):
     out = np.where(finite[..., None], out, 0.0)
     lse = np.where(finite, ref + np.log(safe), -np.inf)
     return out, lse
+
+
+def verify_attention_ragged(q, k_pages, v_pages, page_table, kv_lens, q_lens, q_start, sm_scale,
+                            k_scales=None, v_scales=None, groups=None):
+    """Causal GQA of verify blocks whose width differs per request.
+
+    Request b's block has q_b = q_lens[b] rows, stored at rows
+    q_start[b] .. q_start[b] + q_b - 1 of q / out (the packing of the
+    block-preparation step, see ``block.py``); kv_lens[b] counts the block.
+    Row i of request b, query head h, sees the first kv_lens[b] - q_b + i + 1
+    cache positions, exactly as in ``verify_attention``. Written per row, from
+    the definition at the top of this module.
+
+    Returns (out [rows, Hq, D], lse [rows, Hq]) in float64; rows of groups not
+    requested are NaN.
+    """
+    q = _as_np(q)
+    k_pages, v_pages = _as_np(k_pages), _as_np(v_pages)
+    k_scales, v_scales = _as_np(k_scales), _as_np(v_scales)
+    page_table, kv_lens = _as_np(page_table), _as_np(kv_lens)
+    q_lens, q_start = _as_np(q_lens), _as_np(q_start)
+    rows_total, Hq, D = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    B = len(kv_lens)
+    out = np.full((rows_total, Hq, D), np.nan)
+    lse = np.full((rows_total, Hq), np.nan)
+    todo = [(b, g) for b in range(B) for g in range(Hkv)] if groups is None else list(groups)
+    for b, g in todo:
+        qb, n_all = int(q_lens[b]), int(kv_lens[b])
+        K = gather_kv(k_pages, k_scales, page_table[b], n_all, g)
+        V = gather_kv(v_pages, v_scales, page_table[b], n_all, g)
+        for i in range(qb):
+            r = int(q_start[b]) + i
+            n = n_all - qb + i + 1
+            for j in range(G):
+                h = g * G + j
+                s = sm_scale * (K[:n] @ q[r, h].astype(np.float64))  # [n]
+                m = s.max()
+                w = np.exp(s - m)
+                l = w.sum()
+                out[r, h] = (w @ V[:n]) / l
+                lse[r, h] = m + np.log(l)
+    return out, lse
