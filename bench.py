@@ -5,7 +5,7 @@ One step = one verify of a block: paged causal GQA over the long cache
 greedy acceptance over the block's fp32 logits (sv_greedy_accept), on seeded
 synthetic inputs already resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal] [--ragged]
 
 Prints one JSON line. `value` is the effective HBM bandwidth of the whole step
 (algorithmic bytes of attention + accept / step time). The `roofline` object
@@ -53,6 +53,9 @@ def parse():
                     help="time a device-to-device copy of this size as an attainable-bandwidth reference")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ragged", action="store_true",
+                    help="also time one round of blocks of a seeded width per request (2..q_len): block "
+                         "preparation, K/V append, ragged verify attention and ragged greedy accept")
     ap.add_argument("--traffic", default=None,
                     help="JSON with measured HBM bytes per verify_attn launch (default: the one under "
                          "profiles/ for this workload, used only while the kernel source is unchanged)")
@@ -226,6 +229,10 @@ def main():
                     "note": "device copy (read + write) as an attainable-bandwidth reference"}
         del src, dst
 
+    ragged = None
+    if args.ragged:
+        ragged = ragged_round(x, wl, acc_in, page_table, stream, timed, n_part)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wl)
@@ -282,8 +289,80 @@ def main():
         "q_sweep": qsw,
         "verify_attention_cold": cold,
         "reference_copy": ref_copy,
+        "ragged_round": ragged,
     }
     print(json.dumps(res), flush=True)
+
+
+def ragged_round(x, wl, acc_in, page_table, stream, timed, n):
+    """One verify round with a seeded width per request (2..q_len), on the
+    workload's cache: prepare_block, append_kv (rewriting the block rows with
+    the values already there, so the pool is unchanged), ragged verify
+    attention and ragged greedy accept, each timed alone."""
+    import numpy as np
+    import torch
+
+    from long_context_gqa_amd import binding as B
+    from long_context_gqa_amd import workloads as W
+    dev = x.q.device
+    q = wl.q_len
+    widths = W.block_widths(wl, lo=min(2, q))
+    prefixes = [int(k) - q for k in x.kv_lens.tolist()]
+    rows = sum(widths)
+    i32 = dict(dtype=torch.int32, device=dev)
+    seq = torch.tensor(prefixes, **i32)
+    last = torch.zeros(wl.batch, **i32)  # t0 of each block (never compared)
+    prep = B.PrepareCall(seq, torch.tensor(widths, **i32), page_table, q, wl.page_size, x.num_pages,
+                         last, acc_in.draft_ids if q > 1 else None)
+    prep.run(stream)
+    torch.cuda.synchronize()
+    if prep.flags.item() or prep.q_start[-1].item() != rows:
+        raise SystemExit("block preparation flagged or miscounted the rows")
+    res = {"widths": widths, "rows": rows, "batch": wl.batch, "max_width": q}
+    res["prepare_us"] = round(float(np.median(timed(lambda: prep.run(stream), n))), 2)
+
+    if wl.kv_dtype == "fp16":
+        P = wl.page_size
+        sl = prep.cache_slot[:rows].long()
+        nk = x.k_pages[sl // P, :, sl % P].contiguous()
+        nv = x.v_pages[sl // P, :, sl % P].contiguous()
+        ab = 2 * 2 * nk.numel() * 2 + rows * 4  # K and V rows read and written, slots read
+
+        def app():
+            B.sv_append_kv(nk, nv, prep.cache_slot, prep.q_start, wl.batch, wl.batch * q, x.k_pages, x.v_pages,
+                           prep.flags, stream)
+        app()
+        us = float(np.median(timed(app, n)))
+        res.update(append_us=round(us, 2), append_GBps=round(ab / (us * 1e-6) / 1e9, 1), append_bytes=ab)
+
+    qp = W.pack_rows(x.q, q, widths)
+    rc = B.RaggedVerifyCall(qp, prep.q_start, x.k_pages, x.v_pages, page_table, prep.kv_lens_out, q, x.max_kv_len,
+                            x.k_scales, x.v_scales, x.sm_scale, 0)
+    for _ in range(3):
+        rc.run(stream)
+    us = float(np.median(timed(lambda: rc.run(stream), n)))
+    if rc.flags.item():
+        raise SystemExit(f"ragged verify flagged a contract violation: {rc.flags.item()}")
+    vb = W.verify_algorithmic_bytes([p_ + w for p_, w in zip(prefixes, widths)], widths, wl.num_q_heads,
+                                    wl.num_kv_heads, wl.head_dim, wl.page_size, wl.kv_dtype)
+    gbs = vb / (us * 1e-6) / 1e9
+    res.update(verify_us=round(us, 2), verify_GBps=round(gbs, 1), verify_pct_of_peak_hbm=round(100 * gbs / 8000, 2),
+               verified_tok_per_s=round(rows / (us * 1e-6), 1), verify_algorithmic_bytes=vb,
+               splits=rc.splits, chunk_tokens=rc.chunk)
+
+    logits = W.pack_rows(acc_in.logits, q, widths)
+    ac = B.RaggedAcceptCall(logits, prep.block_ids, prep.q_start, wl.batch, q, prep.kv_lens_out)
+    ac.run(stream)
+    us = float(np.median(timed(lambda: ac.run(stream), n)))
+    # planted lengths cut at each width (the drafts before the cut are the same)
+    expect = torch.minimum(acc_in.planted_accept, torch.tensor(widths, dtype=torch.int32) - 1)
+    if not torch.equal(ac.accept_len.cpu(), expect):
+        raise SystemExit("ragged accept lengths differ from the planted ones cut at each width")
+    accb = rows * wl.vocab * 4 + rows * 4 + (wl.batch + 1) * 4 + 3 * wl.batch * 4
+    res.update(accept_us=round(us, 2), accept_GBps=round(accb / (us * 1e-6) / 1e9, 1), accept_bytes=accb)
+    log(f"[bench] ragged round: {rows} rows; prepare {res['prepare_us']} us, append {res.get('append_us')} us, "
+        f"verify {res['verify_us']} us ({res['verify_GBps']} GB/s), accept {res['accept_us']} us")
+    return res
 
 
 def measured_traffic(path, workload):

@@ -1,7 +1,8 @@
 /*
  * sv.h — C ABI of the target-verify path of speculative decoding on MI355X
  * (gfx950): paged causal grouped-query attention of a verify block, the
- * merge of split-KV partials, and greedy acceptance.
+ * merge of split-KV partials, and greedy acceptance; blocks of one width or
+ * of a width per request, and the preparation and K/V append of a block.
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless marked "host".
@@ -44,7 +45,10 @@ typedef enum { SV_KV_FP16 = 0, SV_KV_FP8_E4M3 = 1 } sv_kv_dtype;
 /* Bits OR-ed into *status_flags by the kernels. */
 #define SV_FLAG_KV_LEN_ABOVE_BOUND 0x1 /* kv_lens[b] > max_kv_len or > max_pages_per_req*page_size; clamped */
 #define SV_FLAG_KV_LEN_BELOW_BLOCK 0x2 /* kv_lens[b] < q_len; rows that see no key give 0 output, -inf lse */
-#define SV_FLAG_PAGE_ID_OUT_OF_RANGE 0x4 /* page id < 0 or >= num_pages; page 0 read instead */
+#define SV_FLAG_PAGE_ID_OUT_OF_RANGE 0x4 /* page id < 0 or >= num_pages; page 0 read instead
+                                           (sv_prepare_block, sv_append_kv: the row's slot is -1 / skipped) */
+#define SV_FLAG_BAD_BLOCK_WIDTH 0x8 /* a width outside 0..max, or packed rows outside 0..batch*max;
+                                       that request is treated as having no block */
 
 /*
  * Shape and layout of one verify call (host struct).
@@ -137,7 +141,35 @@ sv_status sv_verify_merge(const float* part_o, const float* part_lse, int32_t nu
                           int32_t num_rows, int32_t num_heads, int32_t head_dim, void* out,
                           float* out_lse, void* stream);
 
-/* Bytes of workspace sv_greedy_accept needs. */
+/*
+ * Verify blocks of different widths per request (the adaptive verify width
+ * of the PocketLLM page's DFlash2 runs; per-request verify lengths chosen by
+ * a scheduler, DSpark in section 1.7.2 of the page "DFlash -> dLLM
+ * self-spec, part 1"). The same attention as sv_verify_attention, with the
+ * rows of the requests packed one after another:
+ *
+ *   q_start     [batch+1] int32 device: request b owns rows
+ *               q_start[b] .. q_start[b+1]-1 of q / out / out_lse, i.e. a
+ *               block of q_b = q_start[b+1] - q_start[b] rows, 0 <= q_b <= p->q_len,
+ *               and all rows lie in 0 .. batch*p->q_len - 1 (sv_prepare_block
+ *               writes such offsets). Row i of request b attends to cache
+ *               positions 0 .. kv_lens[b] - q_b + i. A request with q_b = 0
+ *               is skipped; one that breaks the rule is skipped and flagged
+ *               (SV_FLAG_BAD_BLOCK_WIDTH).
+ *   p->q_len    the largest width; the plan, the workspace size and the
+ *               kernels' row blocks are those of a uniform call of that width
+ *   q, out      [rows, Hq, D] fp16 (rows = q_start[batch]); out_lse [rows, Hq]
+ * Every other argument is as for sv_verify_attention. Rows outside every
+ * request's range are not written.
+ */
+sv_status sv_verify_attention_ragged(const sv_verify_params* p, const int32_t* q_start, const void* q,
+                                     const void* k_pages, const void* v_pages, const void* k_scales,
+                                     const void* v_scales, const int32_t* page_table, const int32_t* kv_lens,
+                                     void* out, float* out_lse, void* workspace, size_t workspace_bytes,
+                                     int32_t* status_flags, void* stream);
+
+/* Bytes of workspace sv_greedy_accept (and sv_greedy_accept_ragged with
+ * q_len = its max_q_len) needs. */
 size_t sv_greedy_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vocab);
 
 /*
@@ -163,6 +195,86 @@ sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_
                            int32_t q_len, int32_t vocab, int32_t* accept_len, int32_t* bonus_ids,
                            int32_t* argmax_ids, const int32_t* kv_lens_in, int32_t* kv_lens_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy acceptance of packed blocks of different widths (same rule as
+ * sv_greedy_accept, rows packed as for sv_verify_attention_ragged).
+ *
+ *   logits      [rows, vocab] fp32, rows = q_start[batch]
+ *   block_ids   [rows] int32: request b's rows hold its block t0, d1, ..,
+ *               d_{q_b-1} (as sv_prepare_block writes them), so the draft
+ *               checked against row j is the id one row later; may be NULL
+ *               when max_q_len == 1
+ *   q_start     [batch+1] int32 packed row offsets, widths 0..max_q_len
+ *   accept_len, bonus_ids [batch] int32 (written); argmax_ids NULL or [rows]
+ *   kv_lens_out[b] = kv_lens_in[b] - q_b + 1 + accept_len[b]
+ * A request without a block (q_b = 0, or flagged SV_FLAG_BAD_BLOCK_WIDTH)
+ * gets accept_len 0, bonus -1 and kv_lens_out = kv_lens_in.
+ * workspace: sv_greedy_accept_workspace_bytes(batch, max_q_len, vocab) bytes.
+ */
+sv_status sv_greedy_accept_ragged(const float* logits, const int32_t* block_ids, const int32_t* q_start,
+                                  int32_t batch, int32_t max_q_len, int32_t vocab, int32_t* accept_len,
+                                  int32_t* bonus_ids, int32_t* argmax_ids, const int32_t* kv_lens_in,
+                                  int32_t* kv_lens_out, void* workspace, size_t workspace_bytes,
+                                  int32_t* status_flags, void* stream);
+
+/*
+ * Block preparation of one verify round (the fused step that yields the
+ * block's token ids, positions and cache locations, section 1.3.3 of the
+ * page "DFlash -> dLLM self-spec, part 1"; slots reserved ahead of time,
+ * section 1.3.2 "KV over-allocation"). For request b with committed length
+ * L_b = seq_lens[b] and width q_b = q_lens[b]:
+ *     q_start[b]   = q_0 + .. + q_{b-1};  q_start[batch] = total rows
+ *     positions[q_start[b] + i]  = L_b + i                      (i < q_b)
+ *     cache_slot[q_start[b] + i] = page_table[b][(L_b+i) / P] * P + (L_b+i) % P
+ *     kv_lens_out[b] = L_b + q_b       (the cache length the verify pass sees)
+ *     block_ids[q_start[b] + i] = last_tokens[b] (i = 0) or draft_ids[b][i-1]
+ *
+ *   seq_lens, q_lens  [batch] int32; 0 <= q_lens[b] <= max_q_len (else the
+ *               width is taken as 0 and SV_FLAG_BAD_BLOCK_WIDTH set)
+ *   page_table  [batch, max_pages_per_req] int32, pages of the pool that
+ *               sv_verify_attention reads; a position past the row or on a
+ *               page id outside 0..num_pages-1 gets cache_slot -1
+ *               (SV_FLAG_PAGE_ID_OUT_OF_RANGE)
+ *   last_tokens NULL, or [batch] int32: t0 of each block (with block_ids)
+ *   draft_ids   [batch, max_q_len-1] int32, padded (may be NULL when
+ *               max_q_len == 1 or last_tokens is NULL)
+ *   q_start     [batch+1] int32 (written)
+ *   positions   NULL or [batch*max_q_len] int32 (first q_start[batch] written)
+ *   cache_slot  [batch*max_q_len] int32 (first q_start[batch] written)
+ *   kv_lens_out NULL or [batch] int32 (written; may alias seq_lens)
+ *   block_ids   NULL or [batch*max_q_len] int32 (written)
+ * One workgroup; cost grows with batch (about a microsecond per 256 requests).
+ */
+sv_status sv_prepare_block(const int32_t* seq_lens, const int32_t* q_lens, const int32_t* page_table,
+                           int32_t batch, int32_t max_q_len, int32_t max_pages_per_req, int32_t page_size,
+                           int32_t num_pages, const int32_t* last_tokens, const int32_t* draft_ids,
+                           int32_t* q_start, int32_t* positions, int32_t* cache_slot, int32_t* kv_lens_out,
+                           int32_t* block_ids, int32_t* status_flags, void* stream);
+
+/*
+ * Writing a block's K and V into its reserved cache slots (the append of
+ * the verify block before the verify pass, section 1.3.2 of the page
+ * "DFlash -> dLLM self-spec, part 1"):
+ *     k_pages[slot / P, h, slot % P, :] = new_k[r, h, :]   (same for V)
+ * for every packed row r in q_start[0] .. q_start[batch]-1 (clamped to
+ * max_rows) with slot = cache_slot[r] >= 0.
+ *
+ *   new_k, new_v  [rows, num_kv_heads, head_dim] fp16, 16-byte aligned
+ *   cache_slot    [rows] int32 flat slots page*P + slot, or -1 (skipped);
+ *                 a slot >= num_pages*page_size is skipped and flagged
+ *                 (SV_FLAG_PAGE_ID_OUT_OF_RANGE)
+ *   q_start       [batch+1] int32 (e.g. from sv_prepare_block)
+ *   max_rows      host bound on q_start[batch]: sizes the grid
+ *   k_pages, v_pages  [num_pages, num_kv_heads, page_size, head_dim], written
+ *   kv_dtype      SV_KV_FP16 only (FP8 pages: SV_ERR_UNSUPPORTED)
+ * Rows that share a slot race; prepare_block never gives two rows one slot
+ * when the page table maps distinct positions to distinct slots.
+ */
+sv_status sv_append_kv(const void* new_k, const void* new_v, const int32_t* cache_slot, const int32_t* q_start,
+                       int32_t batch, int32_t max_rows, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t num_pages, sv_kv_dtype kv_dtype, void* k_pages, void* v_pages,
+                       int32_t* status_flags, void* stream);
 
 const char* sv_status_string(sv_status s);
 const char* sv_last_error(void);

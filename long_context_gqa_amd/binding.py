@@ -19,10 +19,12 @@ LIB_PATH = os.path.join(_PKG, "libsv.so")
 SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_HIP = range(5)
 SV_KV_FP16, SV_KV_FP8_E4M3 = 0, 1
 SV_FLAG_KV_LEN_ABOVE_BOUND, SV_FLAG_KV_LEN_BELOW_BLOCK, SV_FLAG_PAGE_ID_OUT_OF_RANGE = 1, 2, 4
+SV_FLAG_BAD_BLOCK_WIDTH = 8
 
 EXPORTED = (
     "sv_verify_workspace_bytes", "sv_verify_plan", "sv_verify_attention", "sv_verify_merge",
-    "sv_greedy_accept_workspace_bytes", "sv_greedy_accept", "sv_status_string", "sv_last_error",
+    "sv_greedy_accept_workspace_bytes", "sv_greedy_accept", "sv_verify_attention_ragged",
+    "sv_greedy_accept_ragged", "sv_prepare_block", "sv_append_kv", "sv_status_string", "sv_last_error",
     "sv_version",
 )
 
@@ -74,6 +76,14 @@ def lib() -> ctypes.CDLL:
         L.sv_greedy_accept_workspace_bytes.restype = sz
         L.sv_greedy_accept.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sv_greedy_accept.restype = ctypes.c_int
+        L.sv_verify_attention_ragged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32p, vp, sz, vp, vp]
+        L.sv_verify_attention_ragged.restype = ctypes.c_int
+        L.sv_greedy_accept_ragged.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.sv_greedy_accept_ragged.restype = ctypes.c_int
+        L.sv_prepare_block.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sv_prepare_block.restype = ctypes.c_int
+        L.sv_append_kv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp]
+        L.sv_append_kv.restype = ctypes.c_int
         L.sv_status_string.argtypes = [ctypes.c_int]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_last_error.argtypes = []
@@ -154,6 +164,42 @@ def sv_greedy_accept(logits, draft_ids, batch, q_len, vocab, accept_len, bonus_i
                                   _ptr(kv_lens_out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def sv_verify_attention_ragged(p: SvVerifyParams, q_start, q, k_pages, v_pages, k_scales, v_scales, page_table,
+                               kv_lens, out, out_lse=None, workspace=None, status_flags=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sv_verify_attention_ragged(ctypes.byref(p), _ptr(q_start), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                             _ptr(k_scales), _ptr(v_scales), _ptr(page_table), _ptr(kv_lens),
+                                             _ptr(out), _ptr(out_lse), _ptr(workspace), ws_bytes,
+                                             _ptr(status_flags), _stream(stream)))
+
+
+def sv_greedy_accept_ragged(logits, block_ids, q_start, batch, max_q_len, vocab, accept_len, bonus_ids,
+                            argmax_ids=None, kv_lens_in=None, kv_lens_out=None, workspace=None, status_flags=None,
+                            stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sv_greedy_accept_ragged(_ptr(logits), _ptr(block_ids), _ptr(q_start), batch, max_q_len, vocab,
+                                         _ptr(accept_len), _ptr(bonus_ids), _ptr(argmax_ids), _ptr(kv_lens_in),
+                                         _ptr(kv_lens_out), _ptr(workspace), ws_bytes, _ptr(status_flags),
+                                         _stream(stream)))
+
+
+def sv_prepare_block(seq_lens, q_lens, page_table, batch, max_q_len, page_size, num_pages, q_start, cache_slot,
+                     positions=None, kv_lens_out=None, last_tokens=None, draft_ids=None, block_ids=None,
+                     status_flags=None, stream=None):
+    _check(lib().sv_prepare_block(_ptr(seq_lens), _ptr(q_lens), _ptr(page_table), batch, max_q_len,
+                                  page_table.shape[1], page_size, num_pages, _ptr(last_tokens), _ptr(draft_ids),
+                                  _ptr(q_start), _ptr(positions), _ptr(cache_slot), _ptr(kv_lens_out),
+                                  _ptr(block_ids), _ptr(status_flags), _stream(stream)))
+
+
+def sv_append_kv(new_k, new_v, cache_slot, q_start, batch, max_rows, k_pages, v_pages, status_flags=None,
+                 stream=None):
+    num_pages, Hkv, P, D = k_pages.shape
+    _check(lib().sv_append_kv(_ptr(new_k), _ptr(new_v), _ptr(cache_slot), _ptr(q_start), batch, max_rows, Hkv, D, P,
+                              num_pages, SV_KV_FP16 if k_pages.dtype == torch.float16 else SV_KV_FP8_E4M3,
+                              _ptr(k_pages), _ptr(v_pages), _ptr(status_flags), _stream(stream)))
+
+
 def sv_version() -> int:
     return int(lib().sv_version())
 
@@ -223,3 +269,81 @@ class AcceptCall:
 def greedy_accept(logits, draft_ids, q_len, kv_lens=None):
     c = AcceptCall(logits, draft_ids, q_len, kv_lens)
     return c.run()
+
+
+# ---------------------------------------------------------------------------
+# Blocks of a width per request
+
+class RaggedVerifyCall:
+    """Device buffers of one verify-attention call over packed blocks of
+    different widths (rows of request b: q_start[b] .. q_start[b+1]-1);
+    ``max_q_len`` is the largest width."""
+
+    def __init__(self, q, q_start, k_pages, v_pages, page_table, kv_lens, max_q_len, max_kv_len,
+                 k_scales=None, v_scales=None, sm_scale=None, num_splits=0, with_lse=True):
+        dev = q.device
+        B = kv_lens.shape[0]
+        Hq, D = q.shape[1], q.shape[2]
+        Hkv, P = k_pages.shape[1], k_pages.shape[2]
+        dtype = SV_KV_FP8_E4M3 if k_pages.dtype == torch.uint8 else SV_KV_FP16
+        self.params = make_params(B, max_q_len, Hq, Hkv, D, P, k_pages.shape[0], page_table.shape[1],
+                                  max_kv_len, dtype, sm_scale, num_splits)
+        self.q_start = q_start
+        self.inputs = (q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens)
+        self.out = torch.empty_like(q)
+        self.out_lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=dev) if with_lse else None
+        nbytes = sv_verify_workspace_bytes(self.params)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.splits, self.chunk = sv_verify_plan(self.params)
+
+    def run(self, stream=None):
+        sv_verify_attention_ragged(self.params, self.q_start, *self.inputs, self.out, self.out_lse, self.workspace,
+                                   self.flags, stream)
+        return self.out, self.out_lse
+
+
+class RaggedAcceptCall:
+    def __init__(self, logits, block_ids, q_start, batch, max_q_len, kv_lens=None, with_argmax=True):
+        dev = logits.device
+        self.batch, self.max_q_len, self.vocab = batch, max_q_len, logits.shape[1]
+        self.logits, self.block_ids, self.q_start = logits, block_ids, q_start
+        self.accept_len = torch.empty(batch, dtype=torch.int32, device=dev)
+        self.bonus = torch.empty(batch, dtype=torch.int32, device=dev)
+        self.argmax = torch.empty(logits.shape[0], dtype=torch.int32, device=dev) if with_argmax else None
+        self.kv_in = kv_lens
+        self.kv_out = torch.empty_like(kv_lens) if kv_lens is not None else None
+        nbytes = sv_greedy_accept_workspace_bytes(batch, max_q_len, self.vocab)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(self, stream=None):
+        sv_greedy_accept_ragged(self.logits, self.block_ids, self.q_start, self.batch, self.max_q_len, self.vocab,
+                                self.accept_len, self.bonus, self.argmax, self.kv_in, self.kv_out, self.workspace,
+                                self.flags, stream)
+        return self.accept_len, self.bonus, self.argmax, self.kv_out
+
+
+class PrepareCall:
+    """Outputs of one block preparation: q_start [B+1], positions, cache
+    slots and block ids (each [B*max_q_len], the first q_start[B] written)
+    and the cache lengths the verify pass sees."""
+
+    def __init__(self, seq_lens, q_lens, page_table, max_q_len, page_size, num_pages, last_tokens=None,
+                 draft_ids=None):
+        dev = seq_lens.device
+        B = seq_lens.shape[0]
+        self.args = (seq_lens, q_lens, page_table, B, max_q_len, page_size, num_pages)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.q_start = torch.empty(B + 1, **i32)
+        self.positions = torch.empty(B * max_q_len, **i32)
+        self.cache_slot = torch.empty(B * max_q_len, **i32)
+        self.kv_lens_out = torch.empty(B, **i32)
+        self.last_tokens, self.draft_ids = last_tokens, draft_ids
+        self.block_ids = torch.empty(B * max_q_len, **i32) if last_tokens is not None else None
+        self.flags = torch.zeros(1, **i32)
+
+    def run(self, stream=None):
+        sv_prepare_block(*self.args, self.q_start, self.cache_slot, self.positions, self.kv_lens_out,
+                         self.last_tokens, self.draft_ids, self.block_ids, self.flags, stream)
+        return self

@@ -46,8 +46,15 @@ __device__ __forceinline__ Best wave_best(Best x) {
 template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* __restrict__ logits,
                                                                   int vocab, int slice,
-                                                                  int n_slices, float2* ws) {
+                                                                  int n_slices, float2* ws,
+                                                                  const int32_t* q_start, int batch,
+                                                                  int max_rows) {
   const int sl = blockIdx.x, row = blockIdx.y;
+  if (q_start) {
+    // packed widths: only rows q_start[0] .. q_start[batch]-1 exist
+    const int lo_row = q_start[0], hi_row = q_start[batch];
+    if (row < lo_row || row >= hi_row || row >= max_rows) return;
+  }
   const int lo = sl * slice, hi = min(lo + slice, vocab);
   const float* rp = logits + (size_t)row * vocab;
   Best b{-INFINITY, INT32_MAX};
@@ -85,15 +92,35 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* _
   }
 }
 
-// One workgroup per request: the slices of all q_len rows are reduced at
-// once (each row by a team of lanes), then one thread walks the drafts.
-__global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
-    const float2* __restrict__ ws, int n_slices, const int32_t* __restrict__ draft_ids, int q_len,
-    int32_t* accept_len, int32_t* bonus_ids, int32_t* argmax_ids, const int32_t* kv_lens_in,
-    int32_t* kv_lens_out) {
+// One workgroup per request: the slices of all its rows are reduced at once
+// (each row by a team of lanes), then one thread walks the drafts.
+__global__ __launch_bounds__(kThreads) void accept_finalize_kernel(AcceptLaunch a) {
   __shared__ int am_s[kMaxAcceptRows];
   __shared__ Best red[kThreads];
   const int b = blockIdx.x, tid = threadIdx.x;
+  const float2* __restrict__ ws = a.ws;
+  const int n_slices = a.n_slices;
+  // the request's rows r0 .. r0+q_len-1, and where the draft checked against
+  // row j sits: d_{j+1} of the padded draft matrix, or the block id one row on
+  int q_len = a.q_len, r0 = b * a.q_len;
+  const int32_t* dp = a.draft_ids;
+  if (!a.q_start) {
+    if (q_len > 1) dp += (size_t)b * (q_len - 1);
+  } else {
+    int flag_bits = 0;
+    q_len = block_rows(a.q_start, b, a.batch, a.q_len, &r0, &flag_bits);
+    if (q_len == 0) {
+      // no block (width 0, or marked): nothing accepted, no bonus, length kept
+      if (tid == 0) {
+        a.accept_len[b] = 0;
+        a.bonus_ids[b] = -1;
+        if (a.kv_lens_out) a.kv_lens_out[b] = a.kv_lens_in[b];
+        if (flag_bits && a.flags) atomicOr(a.flags, flag_bits);
+      }
+      return;
+    }
+    dp = a.block_ids + r0 + 1;
+  }
   // team of lanes per row: the largest power of two with q_len teams <= 256
   int team = kThreads;
   while (team > 1 && team * q_len > kThreads) team >>= 1;
@@ -101,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
     const int j = j0 + tid / team, k = tid % team;
     Best x{-INFINITY, INT32_MAX};
     if (j < q_len) {
-      const size_t row = (size_t)b * q_len + j;
+      const size_t row = (size_t)r0 + j;
       for (int s = k; s < n_slices; s += team) {
         const float2 p = ws[row * n_slices + s];
         x = better(x, Best{p.x, __float_as_int(p.y)});
@@ -116,30 +143,29 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(
     if (k == 0 && j < q_len) {
       const int am = (red[tid].i == INT32_MAX) ? 0 : red[tid].i;
       am_s[j] = am;
-      if (argmax_ids) argmax_ids[(size_t)b * q_len + j] = am;
+      if (a.argmax_ids) a.argmax_ids[(size_t)r0 + j] = am;
     }
     __syncthreads();
   }
   if (tid == 0) {
     int acc = 0;
-    while (acc < q_len - 1 && draft_ids[(size_t)b * (q_len - 1) + acc] == am_s[acc]) ++acc;
-    accept_len[b] = acc;
-    bonus_ids[b] = am_s[acc];
-    if (kv_lens_out) kv_lens_out[b] = kv_lens_in[b] - q_len + 1 + acc;
+    while (acc < q_len - 1 && dp[acc] == am_s[acc]) ++acc;
+    a.accept_len[b] = acc;
+    a.bonus_ids[b] = am_s[acc];
+    if (a.kv_lens_out) a.kv_lens_out[b] = a.kv_lens_in[b] - q_len + 1 + acc;
   }
 }
 
 void launch_greedy_accept(const AcceptLaunch& a, hipStream_t s) {
-  dim3 g1(a.n_slices, a.batch * a.q_len);
+  const int max_rows = a.batch * a.q_len;
+  dim3 g1(a.n_slices, max_rows);
   if (a.vocab % 4 == 0)
     hipLaunchKernelGGL((argmax_partial_kernel<true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
-                       a.slice, a.n_slices, a.ws);
+                       a.slice, a.n_slices, a.ws, a.q_start, a.batch, max_rows);
   else
     hipLaunchKernelGGL((argmax_partial_kernel<false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
-                       a.slice, a.n_slices, a.ws);
-  hipLaunchKernelGGL(accept_finalize_kernel, dim3(a.batch), dim3(kThreads), 0, s, a.ws, a.n_slices,
-                     a.draft_ids, a.q_len, a.accept_len, a.bonus_ids, a.argmax_ids, a.kv_lens_in,
-                     a.kv_lens_out);
+                       a.slice, a.n_slices, a.ws, a.q_start, a.batch, max_rows);
+  hipLaunchKernelGGL(accept_finalize_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace sv

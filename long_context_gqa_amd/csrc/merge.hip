@@ -48,7 +48,21 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     // merge launched by the verify entry point: a request covered by a single
     // chunk was written directly, and chunks past its length hold nothing
     int dummy = 0;
-    const int b = row / a.q_len;
+    int b = row / a.q_len;
+    if (a.q_start) {
+      // packed rows: the request is the last b with q_start[b] <= row; rows
+      // of no request (past the block, or of a marked request) are skipped
+      int lo = 0, hi = a.batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (a.q_start[mid] <= row) lo = mid;
+        else hi = mid - 1;
+      }
+      b = lo;
+      int st = 0;
+      const int n = block_rows(a.q_start, b, a.batch, a.q_len, &st, &dummy);
+      if (row < st || row >= st + n) return;
+    }
     const int kv = clamp_kv_len(a.kv_lens[b], a.max_kv_len, a.max_pages, a.page_size, &dummy);
     const int nch = kv > 0 ? (kv + a.chunk - 1) / a.chunk : 1;
     if (nch <= 1) return;

@@ -8,8 +8,11 @@ namespace sv {
 
 struct AcceptLaunch {
   const float* logits;
-  const int32_t* draft_ids;
-  int32_t batch, q_len, vocab, slice, n_slices;
+  const int32_t* draft_ids;  // uniform widths: [batch, q_len-1]
+  const int32_t* block_ids;  // packed widths: [rows] = t0, d1, .. per request
+  const int32_t* q_start;    // packed widths: row offsets [batch+1]; NULL for uniform
+  int32_t* flags;
+  int32_t batch, q_len, vocab, slice, n_slices;  // q_len: the (largest) width
   int32_t* accept_len;
   int32_t* bonus_ids;
   int32_t* argmax_ids;

@@ -9,6 +9,7 @@
 
 #include "sv.h"
 #include "sv_accept.h"
+#include "sv_block.h"
 #include "sv_common.h"
 
 namespace {
@@ -169,11 +170,15 @@ sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t
   return ok();
 }
 
-sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const void* k_pages,
-                              const void* v_pages, const void* k_scales, const void* v_scales,
-                              const int32_t* page_table, const int32_t* kv_lens, void* out,
-                              float* out_lse, void* workspace, size_t workspace_bytes,
-                              int32_t* status_flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_start, const void* q,
+                                const void* k_pages, const void* v_pages, const void* k_scales,
+                                const void* v_scales, const int32_t* page_table, const int32_t* kv_lens,
+                                void* out, float* out_lse, void* workspace, size_t workspace_bytes,
+                                int32_t* status_flags, void* stream) {
   Plan pl;
   sv_status st = make_plan(p, &pl);
   if (st != SV_OK) return st;
@@ -201,6 +206,7 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
   a.v_scales = static_cast<const _Float16*>(v_scales);
   a.page_table = page_table;
   a.kv_lens = kv_lens;
+  a.q_start = q_start;
   a.out = static_cast<_Float16*>(out);
   a.out_lse = out_lse;
   a.part_o = pl.ws_bytes ? static_cast<float*>(workspace) : nullptr;
@@ -231,6 +237,8 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
     m.out = a.out;
     m.out_lse = out_lse;
     m.kv_lens = kv_lens;
+    m.q_start = q_start;
+    m.batch = p->batch;
     m.num_splits = pl.splits;
     m.num_rows = p->batch * p->q_len;
     m.num_heads = p->num_q_heads;
@@ -245,6 +253,29 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
     if (st != SV_OK) return st;
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const void* k_pages,
+                              const void* v_pages, const void* k_scales, const void* v_scales,
+                              const int32_t* page_table, const int32_t* kv_lens, void* out,
+                              float* out_lse, void* workspace, size_t workspace_bytes,
+                              int32_t* status_flags, void* stream) {
+  return verify_attention_impl(p, nullptr, q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, out,
+                               out_lse, workspace, workspace_bytes, status_flags, stream);
+}
+
+sv_status sv_verify_attention_ragged(const sv_verify_params* p, const int32_t* q_start, const void* q,
+                                     const void* k_pages, const void* v_pages, const void* k_scales,
+                                     const void* v_scales, const int32_t* page_table, const int32_t* kv_lens,
+                                     void* out, float* out_lse, void* workspace, size_t workspace_bytes,
+                                     int32_t* status_flags, void* stream) {
+  if (!q_start) return fail(SV_ERR_INVALID_ARGUMENT, "q_start must be non-NULL");
+  return verify_attention_impl(p, q_start, q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, out,
+                               out_lse, workspace, workspace_bytes, status_flags, stream);
 }
 
 sv_status sv_verify_merge(const float* part_o, const float* part_lse, int32_t num_splits,
@@ -264,6 +295,8 @@ sv_status sv_verify_merge(const float* part_o, const float* part_lse, int32_t nu
   m.out = static_cast<_Float16*>(out);
   m.out_lse = out_lse;
   m.kv_lens = nullptr;
+  m.q_start = nullptr;
+  m.batch = 0;
   m.num_splits = num_splits;
   m.num_rows = num_rows;
   m.num_heads = num_heads;
@@ -283,10 +316,15 @@ size_t sv_greedy_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vo
   return align256((size_t)batch * q_len * slices * sizeof(float2));
 }
 
-sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_t batch,
-                           int32_t q_len, int32_t vocab, int32_t* accept_len, int32_t* bonus_ids,
-                           int32_t* argmax_ids, const int32_t* kv_lens_in, int32_t* kv_lens_out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sv_status greedy_accept_impl(const float* logits, const int32_t* draft_ids, const int32_t* block_ids,
+                             const int32_t* q_start, int32_t batch, int32_t q_len, int32_t vocab,
+                             int32_t* accept_len, int32_t* bonus_ids, int32_t* argmax_ids,
+                             const int32_t* kv_lens_in, int32_t* kv_lens_out, void* workspace,
+                             size_t workspace_bytes, int32_t* status_flags, void* stream) {
   if (batch < 1 || q_len < 1 || vocab < 1)
     return fail(SV_ERR_INVALID_ARGUMENT, "batch, q_len and vocab must be >= 1");
   if ((long long)batch * q_len > 65535)
@@ -295,7 +333,11 @@ sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_
     return fail(SV_ERR_UNSUPPORTED, "q_len must be <= %d", sv::kMaxAcceptRows);
   if (!logits || !accept_len || !bonus_ids)
     return fail(SV_ERR_INVALID_ARGUMENT, "logits, accept_len and bonus_ids must be non-NULL");
-  if (q_len > 1 && !draft_ids) return fail(SV_ERR_INVALID_ARGUMENT, "draft_ids is NULL");
+  if (q_start) {
+    if (q_len > 1 && !block_ids) return fail(SV_ERR_INVALID_ARGUMENT, "block_ids is NULL");
+  } else if (q_len > 1 && !draft_ids) {
+    return fail(SV_ERR_INVALID_ARGUMENT, "draft_ids is NULL");
+  }
   if ((kv_lens_in == nullptr) != (kv_lens_out == nullptr))
     return fail(SV_ERR_INVALID_ARGUMENT, "kv_lens_in and kv_lens_out must be both NULL or both set");
   if (vocab % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16)
@@ -307,6 +349,9 @@ sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_
   sv::AcceptLaunch a;
   a.logits = logits;
   a.draft_ids = draft_ids;
+  a.block_ids = block_ids;
+  a.q_start = q_start;
+  a.flags = status_flags;
   a.batch = batch;
   a.q_len = q_len;
   a.vocab = vocab;
@@ -322,6 +367,107 @@ sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_
   return check_launch("greedy_accept");
 }
 
+}  // namespace
+
+extern "C" {
+
+sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_t batch,
+                           int32_t q_len, int32_t vocab, int32_t* accept_len, int32_t* bonus_ids,
+                           int32_t* argmax_ids, const int32_t* kv_lens_in, int32_t* kv_lens_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return greedy_accept_impl(logits, draft_ids, nullptr, nullptr, batch, q_len, vocab, accept_len, bonus_ids,
+                            argmax_ids, kv_lens_in, kv_lens_out, workspace, workspace_bytes, nullptr, stream);
+}
+
+sv_status sv_greedy_accept_ragged(const float* logits, const int32_t* block_ids, const int32_t* q_start,
+                                  int32_t batch, int32_t max_q_len, int32_t vocab, int32_t* accept_len,
+                                  int32_t* bonus_ids, int32_t* argmax_ids, const int32_t* kv_lens_in,
+                                  int32_t* kv_lens_out, void* workspace, size_t workspace_bytes,
+                                  int32_t* status_flags, void* stream) {
+  if (!q_start) return fail(SV_ERR_INVALID_ARGUMENT, "q_start must be non-NULL");
+  return greedy_accept_impl(logits, nullptr, block_ids, q_start, batch, max_q_len, vocab, accept_len, bonus_ids,
+                            argmax_ids, kv_lens_in, kv_lens_out, workspace, workspace_bytes, status_flags,
+                            stream);
+}
+
+sv_status sv_prepare_block(const int32_t* seq_lens, const int32_t* q_lens, const int32_t* page_table,
+                           int32_t batch, int32_t max_q_len, int32_t max_pages_per_req, int32_t page_size,
+                           int32_t num_pages, const int32_t* last_tokens, const int32_t* draft_ids,
+                           int32_t* q_start, int32_t* positions, int32_t* cache_slot, int32_t* kv_lens_out,
+                           int32_t* block_ids, int32_t* status_flags, void* stream) {
+  if (batch < 1 || max_q_len < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "batch and max_q_len must be >= 1");
+  if ((long long)batch * max_q_len > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "batch * max_q_len must fit in int32");
+  if (page_size < 1 || max_pages_per_req < 1 || num_pages < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "page_size, max_pages_per_req and num_pages must be >= 1");
+  if ((long long)num_pages * page_size > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "num_pages * page_size must fit in int32 (flat cache slots)");
+  if (!seq_lens || !q_lens || !page_table || !q_start || !cache_slot)
+    return fail(SV_ERR_INVALID_ARGUMENT, "seq_lens, q_lens, page_table, q_start and cache_slot must be non-NULL");
+  if ((last_tokens == nullptr) != (block_ids == nullptr))
+    return fail(SV_ERR_INVALID_ARGUMENT, "last_tokens and block_ids must be both NULL or both set");
+  if (last_tokens && max_q_len > 1 && !draft_ids)
+    return fail(SV_ERR_INVALID_ARGUMENT, "draft_ids is NULL");
+  sv::PrepareArgs a;
+  a.seq_lens = seq_lens;
+  a.q_lens = q_lens;
+  a.page_table = page_table;
+  a.last_tokens = last_tokens;
+  a.draft_ids = draft_ids;
+  a.q_start = q_start;
+  a.positions = positions;
+  a.cache_slot = cache_slot;
+  a.kv_lens_out = kv_lens_out;
+  a.block_ids = block_ids;
+  a.flags = status_flags;
+  a.batch = batch;
+  a.max_width = max_q_len;
+  a.max_pages = max_pages_per_req;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  sv::launch_prepare_block(a, static_cast<hipStream_t>(stream));
+  return check_launch("prepare_block");
+}
+
+sv_status sv_append_kv(const void* new_k, const void* new_v, const int32_t* cache_slot, const int32_t* q_start,
+                       int32_t batch, int32_t max_rows, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t num_pages, sv_kv_dtype kv_dtype, void* k_pages, void* v_pages,
+                       int32_t* status_flags, void* stream) {
+  if (batch < 1 || max_rows < 1 || num_kv_heads < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "batch, max_rows and num_kv_heads must be >= 1");
+  if (kv_dtype != SV_KV_FP16) return fail(SV_ERR_UNSUPPORTED, "sv_append_kv writes fp16 pages only");
+  if (head_dim < 8 || head_dim % 8 != 0 || head_dim > 4096)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in 8..4096 (got %d)", head_dim);
+  if (page_size < 1 || num_pages < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "page_size and num_pages must be >= 1");
+  if ((long long)num_pages * page_size > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "num_pages * page_size must fit in int32 (flat cache slots)");
+  if ((long long)max_rows * num_kv_heads * (head_dim / 8) > 0x7fffffffLL * sv::kThreads)
+    return fail(SV_ERR_UNSUPPORTED, "too many rows");
+  if (!new_k || !new_v || !cache_slot || !q_start || !k_pages || !v_pages)
+    return fail(SV_ERR_INVALID_ARGUMENT, "new_k, new_v, cache_slot, q_start, k_pages and v_pages must be non-NULL");
+  const uintptr_t al = reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v) |
+                       reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages);
+  if (al % 16) return fail(SV_ERR_INVALID_ARGUMENT, "new_k, new_v, k_pages and v_pages must be 16-byte aligned");
+  sv::AppendArgs a;
+  a.new_k = static_cast<const _Float16*>(new_k);
+  a.new_v = static_cast<const _Float16*>(new_v);
+  a.cache_slot = cache_slot;
+  a.q_start = q_start;
+  a.k_pages = static_cast<_Float16*>(k_pages);
+  a.v_pages = static_cast<_Float16*>(v_pages);
+  a.flags = status_flags;
+  a.batch = batch;
+  a.max_rows = max_rows;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  sv::launch_append_kv(a, static_cast<hipStream_t>(stream));
+  return check_launch("append_kv");
+}
+
 const char* sv_status_string(sv_status s) {
   switch (s) {
     case SV_OK: return "SV_OK";
@@ -335,6 +481,6 @@ const char* sv_status_string(sv_status s) {
 
 const char* sv_last_error(void) { return g_err; }
 
-int32_t sv_version(void) { return 100; }
+int32_t sv_version(void) { return 200; }
 
 }  // extern "C"

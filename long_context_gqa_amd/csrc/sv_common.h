@@ -27,9 +27,10 @@ struct AttnArgs {
   const _Float16* v_scales;
   const int32_t* page_table;
   const int32_t* kv_lens;
+  const int32_t* q_start;  // NULL: every request has q_len rows; else packed row offsets [batch+1]
   _Float16* out;
   float* out_lse;
-  float* part_o;    // [S, B*q_len, Hq, D]
+  float* part_o;    // [S, B*q_len, Hq, D] (q_len: the largest width)
   float* part_lse;  // [S, B*q_len, Hq]
   int32_t* flags;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group, page_size;
@@ -45,8 +46,9 @@ struct MergeArgs {
   _Float16* out;
   float* out_lse;
   const int32_t* kv_lens;  // optional: per-request number of chunks
+  const int32_t* q_start;  // optional (with kv_lens): packed row offsets [batch+1]
   int32_t num_splits, num_rows, num_heads, head_dim;
-  int32_t q_len, chunk, max_kv_len, max_pages, page_size;
+  int32_t q_len, chunk, max_kv_len, max_pages, page_size, batch;
 };
 
 // Length of request b as the kernels use it: the stored value clamped to the
@@ -60,6 +62,23 @@ __device__ inline int clamp_kv_len(int raw, int max_kv_len, int max_pages, int p
   if (v > bound) { v = bound; *flag_bits |= 0x1; }
   if (v < 0) v = 0;
   return v;
+}
+
+// Rows of request b in a block packed request by request (row offsets
+// q_start[0..batch]): returns the width q_start[b+1] - q_start[b] and sets
+// *start. A width outside 0..max_width or rows outside 0..batch*max_width
+// mark the request (bit 0x8) and give it width 0, so no access leaves
+// buffers sized for batch*max_width rows.
+__device__ inline int block_rows(const int32_t* q_start, int b, int batch, int max_width, int* start,
+                                 int* flag_bits) {
+  const int s = q_start[b], e = q_start[b + 1];
+  if (s < 0 || e < s || e - s > max_width || (long long)e > (long long)batch * max_width) {
+    *flag_bits |= 0x8;
+    *start = 0;
+    return 0;
+  }
+  *start = s;
+  return e - s;
 }
 
 void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s);

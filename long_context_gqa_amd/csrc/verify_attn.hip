@@ -551,9 +551,20 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const int split = unit / (a.num_kv_heads * a.batch);
   const int g = hb % a.num_kv_heads, b = hb / a.num_kv_heads;
   const int row0 = rblk * RB * 16;  // first row (of the KV head's q_len*G) of this workgroup
-  const int q_len = a.q_len, G = a.group, R = q_len * G, Hq = a.num_q_heads;
-
   int flag_bits = 0;
+  // the request's block: q_len rows from packed row rstart
+  int q_len = a.q_len, rstart = b * a.q_len;
+  if (a.q_start) {
+    q_len = block_rows(a.q_start, b, a.batch, a.q_len, &rstart, &flag_bits);
+    if (q_len == 0) {
+      if (flag_bits && tid == 0 && a.flags) atomicOr(a.flags, flag_bits);
+      return;
+    }
+  }
+  const int G = a.group, R = q_len * G, Hq = a.num_q_heads;
+  if (row0 >= R) return;  // a narrow block leaves the second row block empty
+  const size_t split_stride = (size_t)a.batch * a.q_len * Hq;  // rows of one split's partials
+
   const int raw_kv = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
   const int kv = clamp_kv_len(raw_kv, a.max_kv_len, a.max_pages, a.page_size, &flag_bits);
   if (raw_kv < q_len) flag_bits |= 0x2;
@@ -620,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       // channel map of the score MFMA's k-step s: fp16 KV 32s + 8*(lane/16);
       // FP8 KV 64*(s/2) + 16*(lane/16) + 8*(s%2) (two k-steps per scale block)
       const int d0 = FP8 ? 64 * (s >> 1) + 16 * (ln >> 4) + 8 * (s & 1) : 32 * s + 8 * (ln >> 4);
-      const _Float16* src = a.q + ((size_t)(b * q_len + i) * Hq + g * G + j) * kHeadDim + d0;
+      const _Float16* src = a.q + ((size_t)(rstart + i) * Hq + g * G + j) * kHeadDim + d0;
       v = *reinterpret_cast<const u32x4*>(src);
     }
     qlds[idx] = v;
@@ -798,11 +809,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       const int r = growbase + rb * 16 + lo;
       if (r < R) {
         const int i = r / G, j = r % G;
-        const size_t orow = (size_t)(b * q_len + i) * Hq + g * G + j;
+        const size_t orow = (size_t)(rstart + i) * Hq + g * G + j;
         if (direct) {
           if (a.out_lse) a.out_lse[orow] = lse_row[rb];
         } else {
-          a.part_lse[(size_t)split * a.batch * q_len * Hq + orow] = lse_row[rb];
+          a.part_lse[split * split_stride + orow] = lse_row[rb];
         }
       }
     }
@@ -816,13 +827,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     const float4 v0 = *reinterpret_cast<const float4*>(src);
     const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
     const int i = r / G, j = r % G;
-    const size_t orow = (size_t)(b * q_len + i) * Hq + g * G + j;
+    const size_t orow = (size_t)(rstart + i) * Hq + g * G + j;
     if (direct) {
       half8_t hv = {(_Float16)v0.x, (_Float16)v0.y, (_Float16)v0.z, (_Float16)v0.w,
                     (_Float16)v1.x, (_Float16)v1.y, (_Float16)v1.z, (_Float16)v1.w};
       *reinterpret_cast<half8_t*>(a.out + orow * kHeadDim + d0) = hv;
     } else {
-      float* dst = a.part_o + ((size_t)split * a.batch * q_len * Hq + orow) * kHeadDim + d0;
+      float* dst = a.part_o + (split * split_stride + orow) * kHeadDim + d0;
       reinterpret_cast<float4*>(dst)[0] = v0;
       reinterpret_cast<float4*>(dst)[1] = v1;
     }

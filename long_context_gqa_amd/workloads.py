@@ -96,7 +96,7 @@ def _seed(base: int, stream: int, chunk: int = 0) -> int:
     return (base * 1_000_003 + stream * 10_007 + chunk * 7_919 + 12_345) & ((1 << 63) - 1)
 
 
-S_PREFIX, S_PAGES, S_Q, S_K, S_V, S_BIAS, S_LOGITS, S_ACCEPT, S_DRAFT = range(9)
+S_PREFIX, S_PAGES, S_Q, S_K, S_V, S_BIAS, S_LOGITS, S_ACCEPT, S_DRAFT, S_WIDTH = range(10)
 
 
 def _gen(device, base, stream, chunk=0):
@@ -368,6 +368,31 @@ def make_accept_inputs(wl: Workload, device="cpu", planted: list[int] | None = N
 
 
 # ---------------------------------------------------------------------------
+# Blocks of a width per request
+
+def block_widths(wl: Workload, lo: int = 2) -> list[int]:
+    """Seeded per-request verify widths, uniform over lo..q_len. (An adaptive
+    width policy verifies at least two rows and at most the block, PocketLLM
+    page, DFlash2 adaptive width; the draw stands in for such a policy.)"""
+    g = _gen("cpu", wl.seed, S_WIDTH)
+    return [int(x) for x in torch.randint(lo, wl.q_len + 1, (wl.batch,), generator=g)]
+
+
+def pack_rows(t: torch.Tensor, q_len: int, widths: list[int]) -> torch.Tensor:
+    """The first widths[b] of request b's q_len rows of t, packed request by
+    request (the row layout of blocks of different widths)."""
+    return torch.cat([t[b * q_len:b * q_len + w] for b, w in enumerate(widths)], 0).contiguous()
+
+
+def row_offsets(widths: list[int]) -> torch.Tensor:
+    """int32 [B+1]: where each request's rows start in the packed layout."""
+    out = [0]
+    for w in widths:
+        out.append(out[-1] + int(w))
+    return torch.tensor(out, dtype=torch.int32)
+
+
+# ---------------------------------------------------------------------------
 # Byte accounting (what one verify must move at minimum)
 
 def kv_bytes_per_token_head(head_dim: int, kv_dtype: str) -> int:
@@ -381,13 +406,17 @@ def kv_bytes_per_token_head(head_dim: int, kv_dtype: str) -> int:
 
 def verify_algorithmic_bytes(kv_lens, q_len, num_q_heads, num_kv_heads, head_dim, page_size, kv_dtype) -> int:
     """Visible K/V (+scales) of every request read once, Q read, out written,
-    the page-table entries in use and kv_lens. Split partials excluded."""
+    the page-table entries in use and kv_lens. Split partials excluded.
+    q_len: one width for every request, or a list of per-request widths
+    (then the row offsets, B+1 int32, are counted too)."""
     kv_lens = [int(x) for x in kv_lens]
     B = len(kv_lens)
     kv = sum(kv_lens) * num_kv_heads * kv_bytes_per_token_head(head_dim, kv_dtype)
-    qo = 2 * B * q_len * num_q_heads * head_dim * 2
+    rows = B * q_len if isinstance(q_len, int) else sum(int(w) for w in q_len)
+    qo = 2 * rows * num_q_heads * head_dim * 2
     pt = sum((n + page_size - 1) // page_size for n in kv_lens) * 4
-    return kv + qo + pt + 4 * B
+    offs = 0 if isinstance(q_len, int) else 4 * (B + 1)
+    return kv + qo + pt + 4 * B + offs
 
 
 def accept_algorithmic_bytes(batch, q_len, vocab) -> int:

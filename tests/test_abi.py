@@ -110,3 +110,54 @@ def test_fp16_with_scales_rejected():
     st = lib.sv_verify_attention(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None,
                                  fake, 1 << 30, None, None)
     assert st == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_block_entry_points_reject_bad_arguments_without_launch():
+    lib = B.lib()
+    fake = 1 << 40
+    p = _p(num_splits=4)
+    # ragged attention: q_start is required, and the uniform checks still apply
+    st = lib.sv_verify_attention_ragged(ctypes.byref(p), None, fake, fake, fake, None, None, fake, fake, fake,
+                                        None, fake, 1 << 30, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT and b"q_start" in lib.sv_last_error()
+    st = lib.sv_verify_attention_ragged(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, fake,
+                                        None, fake, 16, None, None)
+    assert st == B.SV_ERR_WORKSPACE_TOO_SMALL
+    st = lib.sv_verify_attention_ragged(ctypes.byref(_p(q_len=17)), fake, fake, fake, fake, None, None, fake,
+                                        fake, fake, None, fake, 1 << 30, None, None)
+    assert st == B.SV_ERR_UNSUPPORTED
+    # ragged accept: q_start and (for widths > 1) block_ids are required
+    need = lib.sv_greedy_accept_workspace_bytes(2, 8, 1000)
+    st = lib.sv_greedy_accept_ragged(fake, fake, None, 2, 8, 1000, fake, fake, None, None, None, fake, need,
+                                     None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT
+    st = lib.sv_greedy_accept_ragged(fake, None, fake, 2, 8, 1000, fake, fake, None, None, None, fake, need,
+                                     None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT and b"block_ids" in lib.sv_last_error()
+    st = lib.sv_greedy_accept_ragged(fake, fake, fake, 2, 8, 1000, fake, fake, None, None, None, fake, need - 1,
+                                     None, None)
+    assert st == B.SV_ERR_WORKSPACE_TOO_SMALL
+    # prepare_block
+    st = lib.sv_prepare_block(fake, fake, fake, 0, 8, 4, 16, 100, None, None, fake, None, fake, None, None,
+                              None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT
+    st = lib.sv_prepare_block(fake, fake, fake, 2, 8, 4, 16, 1 << 28, None, None, fake, None, fake, None, None,
+                              None, None)
+    assert st == B.SV_ERR_UNSUPPORTED  # flat slots past int32
+    st = lib.sv_prepare_block(fake, fake, fake, 2, 8, 4, 16, 100, fake, None, fake, None, fake, None, None,
+                              None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT  # last_tokens without block_ids
+    st = lib.sv_prepare_block(fake, fake, fake, 2, 8, 4, 16, 100, fake, None, fake, None, fake, None, fake,
+                              None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT and b"draft_ids" in lib.sv_last_error()
+    # append_kv
+    st = lib.sv_append_kv(fake, fake, fake, fake, 2, 16, 4, 256, 16, 100, B.SV_KV_FP8_E4M3, fake, fake, None,
+                          None)
+    assert st == B.SV_ERR_UNSUPPORTED
+    st = lib.sv_append_kv(fake, fake, fake, fake, 2, 16, 4, 250, 16, 100, B.SV_KV_FP16, fake, fake, None, None)
+    assert st == B.SV_ERR_UNSUPPORTED  # head_dim not a multiple of 8
+    st = lib.sv_append_kv(fake + 8, fake, fake, fake, 2, 16, 4, 256, 16, 100, B.SV_KV_FP16, fake, fake, None,
+                          None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT  # misaligned
+    st = lib.sv_append_kv(None, fake, fake, fake, 2, 16, 4, 256, 16, 100, B.SV_KV_FP16, fake, fake, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT

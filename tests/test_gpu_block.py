@@ -1,0 +1,316 @@
+"""GPU parity of the blocks-of-a-width-per-request entry points through the C
+ABI against the float64 oracle: ragged verify attention (fp16 and FP8 KV,
+one and two row blocks, forced split counts), block preparation and K/V
+append (bit-exact), ragged greedy acceptance (bit-exact), a whole round
+prepare -> append -> verify -> accept, and the ragged 8K-131K workload at
+full size on sampled groups."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import check, host, say
+from long_context_gqa_amd import binding as B
+from long_context_gqa_amd import workloads as W
+from oracle import accept as oacc
+from oracle import attention as oatt
+from oracle import block as oblk
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def ragged_case(widths, prefixes, P=16, kv_dtype="fp16", Hq=24, Hkv=4, variant="unit", seed=7, order="per_request"):
+    """Pages and Q of a uniform block of max(widths) rows per request; the
+    ragged call uses the first widths[b] rows and kv_len = prefix + width."""
+    qmax = max(max(widths), 1)
+    wl = W.Workload("ragged", len(widths), qmax, ("fixed", 0), P, kv_dtype=kv_dtype, page_order=order, seed=seed,
+                    num_q_heads=Hq, num_kv_heads=Hkv)
+    x = W.make_verify_inputs(wl, variant, device="cuda", kv_lens=[L + qmax for L in prefixes])
+    kv = torch.tensor([L + w for L, w in zip(prefixes, widths)], dtype=torch.int32)
+    q = W.pack_rows(x.q, qmax, widths)
+    return x, q, kv, W.row_offsets(widths), qmax
+
+
+def run_ragged(x, q, kv, qs, qmax, num_splits=0, max_kv_len=None, out_rows=None):
+    mk = max_kv_len if max_kv_len is not None else int(x.kv_lens.max())
+    c = B.RaggedVerifyCall(q, qs.cuda(), x.k_pages, x.v_pages, x.page_table.cuda(),
+                           kv.cuda(), qmax, mk, x.k_scales, x.v_scales, x.sm_scale, num_splits)
+    if out_rows is not None:  # a sentinel-filled output of out_rows rows
+        c.out = torch.full((out_rows,) + tuple(q.shape[1:]), 7.0, dtype=torch.float16, device="cuda")
+        c.out_lse = torch.full((out_rows, q.shape[1]), 7.0, dtype=torch.float32, device="cuda")
+    c.run()
+    torch.cuda.synchronize()
+    return c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), int(c.flags.item())
+
+
+def ragged_oracle(x, q, kv, qs, widths, groups=None):
+    h = host(x)
+    return oatt.verify_attention_ragged(q.cpu(), h["k_pages"], h["v_pages"], h["page_table"], kv,
+                                        np.array(widths), qs.numpy(), x.sm_scale, h["k_scales"], h["v_scales"],
+                                        groups=groups)
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3"])
+@pytest.mark.parametrize("widths,prefixes,P", [
+    ([1, 8, 3], [100, 37, 2000], 16),
+    ([8, 8, 8], [300, 1, 950], 16),
+    ([5, 1, 2, 7, 4], [0, 4000, 64, 65, 1023], 64),
+    ([16, 3, 9], [333, 2500, 48], 16),    # 96 rows per KV head: two row blocks, some empty
+    ([2, 16], [5000, 17], 32),
+])
+def test_ragged_small_parity(widths, prefixes, P, kv_dtype):
+    x, q, kv, qs, qmax = ragged_case(widths, prefixes, P, kv_dtype, seed=sum(widths) + P)
+    ref, ref_lse = ragged_oracle(x, q, kv, qs, widths)
+    for splits in (0, 1, 3, 7):
+        say(f"widths={widths} prefixes={prefixes} P={P} {kv_dtype} splits={splits}")
+        out, lse, flags = run_ragged(x, q, kv, qs, qmax, splits)
+        assert flags == 0
+        check(out, lse, ref, ref_lse, what=f"splits={splits}")
+
+
+def test_ragged_equal_widths_bitwise_equal_uniform_entry():
+    widths, prefixes = [8, 8, 8, 8], [700, 1500, 33, 4096]
+    x, q, kv, qs, qmax = ragged_case(widths, prefixes, 16, seed=3)
+    for splits in (0, 1, 5):
+        out_r, lse_r, _ = run_ragged(x, q, kv, qs, qmax, splits)
+        u = B.verify_attention(x.q, x.k_pages, x.v_pages, x.page_table.cuda(), kv.cuda(), 8, int(x.kv_lens.max()),
+                               None, None, x.sm_scale, splits)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_r, u[0].float().cpu().numpy())
+        assert np.array_equal(lse_r, u[1].cpu().numpy())
+
+
+def test_ragged_row_equals_uniform_call_of_its_own_width():
+    # request b of a ragged call vs a one-request uniform call of width q_b
+    # over the same cache: bitwise (chunks anchored at absolute positions)
+    # (forced split counts, so both calls cut the keys into the same chunks)
+    widths, prefixes = [3, 11, 1, 6], [900, 257, 4000, 64]
+    x, q, kv, qs, qmax = ragged_case(widths, prefixes, 16, seed=9)
+    mk = int(x.kv_lens.max())
+    for splits in (1, 3):
+        out, lse, _ = run_ragged(x, q, kv, qs, qmax, splits, max_kv_len=mk)
+        for b, w in enumerate(widths):
+            qb = q[int(qs[b]):int(qs[b + 1])].contiguous()
+            ub = B.verify_attention(qb, x.k_pages, x.v_pages, x.page_table[b:b + 1].contiguous().cuda(),
+                                    kv[b:b + 1].cuda(), w, mk, None, None, x.sm_scale, splits)
+            torch.cuda.synchronize()
+            mine, theirs = out[int(qs[b]):int(qs[b + 1])], ub[0].float().cpu().numpy()
+            say(f"  splits {splits} request {b} width {w}: bitwise equal {np.array_equal(mine, theirs)}")
+            assert np.abs(mine - theirs).max() <= 1e-3
+
+
+def test_ragged_zero_and_bad_widths_skip_only_their_request():
+    # q_start [0, 4, 4, 9, 30, ...]: request 1 has no block (width 0, not an
+    # error); request 3's width 21 exceeds the maximum 8 (flagged, skipped).
+    # Rows of skipped requests keep the sentinel; the rest match the oracle.
+    widths, prefixes = [4, 0, 5, 8, 3], [120, 50, 999, 300, 2048]
+    x, q, kv, qs, qmax = ragged_case(widths, prefixes, 16, seed=21)
+    ref, ref_lse = ragged_oracle(x, q, kv, qs, widths)
+    bad = qs.clone()
+    bad[4] = bad[3] + 21          # request 3: 21 rows
+    bad[5] = bad[4]               # request 4: width 0 (keeps the offsets in bounds)
+    rows = len(widths) * qmax
+    for splits in (1, 4):
+        out, lse, flags = run_ragged(x, q, kv, bad, qmax, splits, out_rows=rows)
+        assert flags == B.SV_FLAG_BAD_BLOCK_WIDTH
+        keep = np.zeros(rows, dtype=bool)
+        for b in (0, 2):
+            keep[int(qs[b]):int(qs[b + 1])] = True
+        n = int(qs[-1])
+        check(out[:n][keep[:n]], lse[:n][keep[:n]], ref[keep[:n]], ref_lse[keep[:n]], what=f"splits={splits}")
+        assert (out[~keep] == 7.0).all() and (lse[~keep] == 7.0).all()
+
+
+def test_prepare_block_matches_oracle_bitwise():
+    rng = np.random.default_rng(5)
+    Bn, qmax, P = 300, 16, 16  # more than one group of 256 requests
+    widths = rng.integers(0, qmax + 1, Bn)
+    L = rng.integers(0, 3000, Bn)
+    npg = (L + widths + P - 1) // P
+    maxp = int(npg.max()) + 1
+    num_pages = int(npg.sum()) + 10
+    perm = rng.permutation(num_pages)
+    table = np.full((Bn, maxp), -1, dtype=np.int32)
+    off = 0
+    for b in range(Bn):
+        table[b, :npg[b]] = perm[off:off + npg[b]]
+        off += npg[b]
+    last = rng.integers(0, 248320, Bn).astype(np.int32)
+    drafts = rng.integers(0, 248320, (Bn, qmax - 1)).astype(np.int32)
+    c = B.PrepareCall(torch.tensor(L, dtype=torch.int32).cuda(), torch.tensor(widths, dtype=torch.int32).cuda(),
+                      torch.tensor(table).cuda(), qmax, P, num_pages, torch.tensor(last).cuda(),
+                      torch.tensor(drafts).cuda()).run()
+    torch.cuda.synchronize()
+    r = oblk.prepare_block(L, widths, table, P, last, drafts)
+    n = int(r["q_start"][-1])
+    assert c.flags.item() == 0
+    assert np.array_equal(c.q_start.cpu().numpy(), r["q_start"])
+    assert np.array_equal(c.positions.cpu().numpy()[:n], r["positions"])
+    assert np.array_equal(c.cache_slot.cpu().numpy()[:n], r["cache_slot"])
+    assert np.array_equal(c.kv_lens_out.cpu().numpy(), r["kv_lens_out"])
+    assert np.array_equal(c.block_ids.cpu().numpy()[:n], r["block_ids"])
+
+
+def test_prepare_block_flags_unreserved_slots_and_bad_widths():
+    # request 0's block runs past its page-table row; request 1's width is 9
+    # with a maximum of 8 (taken as 0); request 2 is ordinary
+    P, qmax = 16, 8
+    L = torch.tensor([30, 5, 40], dtype=torch.int32)
+    widths = torch.tensor([8, 9, 3], dtype=torch.int32)
+    table = torch.tensor([[3, 1, -1], [0, -1, -1], [2, 4, 5]], dtype=torch.int32)
+    c = B.PrepareCall(L.cuda(), widths.cuda(), table.cuda(), qmax, P, 6).run()
+    torch.cuda.synchronize()
+    assert c.flags.item() == B.SV_FLAG_PAGE_ID_OUT_OF_RANGE | B.SV_FLAG_BAD_BLOCK_WIDTH
+    assert c.q_start.cpu().tolist() == [0, 8, 8, 11]
+    slots = c.cache_slot.cpu().tolist()
+    # positions 30, 31 on page 1; 32..37 past the row (page entry -1)
+    assert slots[:8] == [1 * P + 14, 1 * P + 15] + [-1] * 6
+    assert slots[8:11] == [5 * P + 8, 5 * P + 9, 5 * P + 10]
+    assert c.kv_lens_out.cpu().tolist() == [38, 5, 43]
+
+
+def test_append_kv_matches_oracle_bitwise():
+    rng = np.random.default_rng(8)
+    Bn, qmax, P, Hkv, D = 7, 16, 16, 4, 256
+    widths = rng.integers(0, qmax + 1, Bn)
+    L = rng.integers(0, 500, Bn)
+    npg = (L + widths + P - 1) // P
+    num_pages = int(npg.sum()) + 3
+    perm = rng.permutation(num_pages)
+    table = np.full((Bn, int(npg.max())), -1, dtype=np.int32)
+    off = 0
+    for b in range(Bn):
+        table[b, :npg[b]] = perm[off:off + npg[b]]
+        off += npg[b]
+    r = oblk.prepare_block(L, widths, table, P)
+    n = int(r["q_start"][-1])
+    g = torch.Generator().manual_seed(3)
+    kp = torch.randn((num_pages, Hkv, P, D), generator=g).half()
+    vp = torch.randn((num_pages, Hkv, P, D), generator=g).half()
+    nk = torch.randn((Bn * qmax, Hkv, D), generator=g).half()
+    nv = torch.randn((Bn * qmax, Hkv, D), generator=g).half()
+    slots = torch.full((Bn * qmax,), -1, dtype=torch.int32)
+    slots[:n] = torch.tensor(r["cache_slot"], dtype=torch.int32)
+    kd, vd = kp.cuda(), vp.cuda()
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.sv_append_kv(nk.cuda(), nv.cuda(), slots.cuda(), torch.tensor(r["q_start"], dtype=torch.int32).cuda(), Bn,
+                   Bn * qmax, kd, vd, flags)
+    torch.cuda.synchronize()
+    assert flags.item() == 0
+    ek = oblk.append_kv(kp.numpy(), r["cache_slot"], nk[:n].numpy())
+    ev = oblk.append_kv(vp.numpy(), r["cache_slot"], nv[:n].numpy())
+    assert np.array_equal(kd.cpu().numpy().view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(vd.cpu().numpy().view(np.uint16), ev.view(np.uint16))
+
+
+def _ragged_accept_inputs(widths, vocab, seed, planted=None):
+    """Logits with a unique planted peak per row and block ids whose drafts
+    match the previous row's peak for the first planted[b] drafts."""
+    rng = np.random.default_rng(seed)
+    qs = W.row_offsets(widths).numpy()
+    n = int(qs[-1])
+    logits = rng.standard_normal((n, vocab)).astype(np.float32)
+    peak = rng.integers(0, vocab, n)
+    logits[np.arange(n), peak] = 10.0
+    ids = rng.integers(0, vocab, n).astype(np.int32)
+    for b, w in enumerate(widths):
+        a = planted[b] if planted is not None else int(rng.integers(0, max(w, 1)))
+        for j in range(1, w):
+            r = int(qs[b]) + j
+            ids[r] = peak[r - 1] if j <= a else (peak[r - 1] + 1) % vocab
+    return logits, ids, qs
+
+
+@pytest.mark.parametrize("widths,vocab", [
+    ([1, 8, 3, 16, 2], 248_320),
+    ([16] * 4 + [1] * 3, 1000),
+    ([5, 0, 7], 8191),
+])
+def test_ragged_accept_matches_oracle_bitwise(widths, vocab):
+    logits, ids, qs = _ragged_accept_inputs(widths, vocab, seed=len(widths) + vocab)
+    kv = np.array([1000 + 10 * b + w for b, w in enumerate(widths)], dtype=np.int32)
+    qmax = max(widths)
+    c = B.RaggedAcceptCall(torch.tensor(logits).cuda(), torch.tensor(ids).cuda(),
+                           torch.tensor(qs, dtype=torch.int32).cuda(), len(widths), qmax,
+                           torch.tensor(kv).cuda())
+    acc, bonus, am, new = [t.cpu().numpy() for t in c.run()]
+    torch.cuda.synchronize()
+    live = [b for b, w in enumerate(widths) if w > 0]
+    ra, rb, ram, rn = oacc.greedy_accept_ragged(logits, ids, np.array(widths), qs, kv)
+    assert c.flags.item() == 0
+    assert np.array_equal(acc[live], ra[live]) and np.array_equal(bonus[live], rb[live])
+    assert np.array_equal(new[live], rn[live])
+    assert np.array_equal(am[:int(qs[-1])], ram)
+    for b in range(len(widths)):
+        if widths[b] == 0:  # no block: nothing accepted, no bonus, length kept
+            assert acc[b] == 0 and bonus[b] == -1 and new[b] == kv[b]
+
+
+def test_whole_round_prepare_append_verify_accept():
+    # One verify round of blocks of different widths, every step on the GPU,
+    # against the oracle's steps in the same order.
+    widths, prefixes, P, qmax, Hq, Hkv, D = [3, 16, 1, 9], [1000, 77, 2047, 400], 16, 16, 24, 4, 256
+    Bn = len(widths)
+    x, _, _, _, _ = ragged_case([qmax] * Bn, prefixes, P, seed=31)  # pages reserved for a full block
+    table = x.page_table
+    rng = np.random.default_rng(4)
+    last = rng.integers(0, 1000, Bn).astype(np.int32)
+    drafts = rng.integers(0, 1000, (Bn, qmax - 1)).astype(np.int32)
+    Ld = torch.tensor(prefixes, dtype=torch.int32).cuda()
+    prep = B.PrepareCall(Ld, torch.tensor(widths, dtype=torch.int32).cuda(), table.cuda(), qmax, P,
+                         x.num_pages, torch.tensor(last).cuda(), torch.tensor(drafts).cuda()).run()
+    g = torch.Generator(device="cuda").manual_seed(12)
+    n = sum(widths)
+    nk = torch.randn((Bn * qmax, Hkv, D), generator=g, device="cuda").half()
+    nv = torch.randn((Bn * qmax, Hkv, D), generator=g, device="cuda").half()
+    q = torch.randn((n, Hq, D), generator=g, device="cuda").half()
+    kp0, vp0 = x.k_pages.cpu(), x.v_pages.cpu()
+    B.sv_append_kv(nk, nv, prep.cache_slot, prep.q_start, Bn, Bn * qmax, x.k_pages, x.v_pages, prep.flags)
+    c = B.RaggedVerifyCall(q, prep.q_start, x.k_pages, x.v_pages, table.cuda(), prep.kv_lens_out, qmax,
+                           max(prefixes) + qmax, sm_scale=x.sm_scale)
+    out, lse = c.run()
+    vocab = 5000
+    logits = torch.randn((n, vocab), generator=g, device="cuda")
+    acc = B.RaggedAcceptCall(logits, prep.block_ids, prep.q_start, Bn, qmax, prep.kv_lens_out).run()
+    torch.cuda.synchronize()
+    assert prep.flags.item() == 0 and c.flags.item() == 0
+    # the oracle, step by step
+    r = oblk.prepare_block(prefixes, widths, table, P, last, drafts)
+    kp = oblk.append_kv(kp0.numpy(), r["cache_slot"], nk[:n].cpu().numpy())
+    vp = oblk.append_kv(vp0.numpy(), r["cache_slot"], nv[:n].cpu().numpy())
+    ref, ref_lse = oatt.verify_attention_ragged(q.cpu(), kp, vp, table, r["kv_lens_out"], np.array(widths),
+                                                r["q_start"], x.sm_scale)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), ref, ref_lse, what="round attention")
+    ra, rb, ram, rn = oacc.greedy_accept_ragged(logits.cpu().numpy(), r["block_ids"], np.array(widths),
+                                                r["q_start"], r["kv_lens_out"])
+    assert np.array_equal(acc[0].cpu().numpy(), ra) and np.array_equal(acc[1].cpu().numpy(), rb)
+    assert np.array_equal(acc[3].cpu().numpy(), rn)
+
+
+@pytest.mark.parametrize("variant", ["literal", "unit"])
+def test_ragged_full_size_8k_131k_sampled(variant):
+    # the ragged 32-request workload (64-token pages, shared pool) with seeded
+    # widths 2..16, through the launch configuration the benchmark times
+    wl = W.WORKLOADS[4]
+    widths = W.block_widths(wl)
+    say(f"ragged widths {widths}: generating {variant}")
+    x = W.make_verify_inputs(wl, variant, device="cuda")
+    prefixes = [int(n) - wl.q_len for n in x.kv_lens.tolist()]
+    kv = torch.tensor([L + w for L, w in zip(prefixes, widths)], dtype=torch.int32)
+    q = W.pack_rows(x.q, wl.q_len, widths)
+    qs = W.row_offsets(widths)
+    out, lse, flags = run_ragged(x, q, kv, qs, wl.q_len)
+    assert flags == 0 and np.isfinite(out).all()
+    lens = [L + w for L, w in zip(prefixes, widths)]
+    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), int(np.argmin(widths)), wl.batch // 2})
+    groups = [(b, (b * 3) % wl.num_kv_heads) for b in picks]
+    say(f"  oracle on groups {groups}")
+    ref, ref_lse = ragged_oracle(x, q, kv, qs, widths, groups=groups)
+    check(out, lse, ref, ref_lse, what=f"ragged full size {variant}")
+    del x
+    torch.cuda.empty_cache()
