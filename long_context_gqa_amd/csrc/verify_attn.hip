@@ -168,6 +168,84 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
     pb[rb] = half4_t{(_Float16)p[rb][0], (_Float16)p[rb][1], (_Float16)p[rb][2], (_Float16)p[rb][3]};
 }
 
+// The pieces of one step for the software-pipelined fp16 loop, where the PV
+// matrix ops of step k are issued right after the score matrix ops of step
+// k+1, and the softmax of k+1 fills their shadow:
+//   scores_mfma   the scaled scores of step k+1 (Q read from LDS with one
+//                 wait per row block);
+//   mask_check    causal/tail masking without branches (per-row limits are
+//                 computed once), each lane's own max, and whether any lane
+//                 needs its row's reference moved;
+//   move_ref      (rare) the row max across the row's four lanes and the new
+//                 reference; alpha is the factor O and l must take;
+//   softmax_p     p at the current reference, its sum, and the fp16 P^T
+//                 fragments (computed before the branch, so they overlap the
+//                 matrix ops; redone after a move);
+//   rescale_o     (rare) O *= alpha, after step k's PV was accumulated at the
+//                 old reference.
+template <int RB>
+__device__ __forceinline__ bool mask_check(float (&x)[RB][4], float (&lmx)[RB], const WaveState<RB>& ws,
+                                           const int (&rowlim)[RB], int lane, int t0) {
+  const int tok = t0 + 4 * (lane >> 4);
+  bool bump = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[rb][i] = (tok + i >= rowlim[rb]) ? -INFINITY : x[rb][i];
+    lmx[rb] = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
+    bump = bump || (lmx[rb] > ws.m[rb] + kLazyLog2);
+  }
+  return __any(bump);
+}
+
+template <int RB>
+__device__ __forceinline__ void move_ref(const float (&lmx)[RB], WaveState<RB>& ws, float (&alpha)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float mx = lmx[rb];
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool bump = mx > ws.m[rb] + kLazyLog2;
+    const float mnew = bump ? mx : ws.m[rb];
+    alpha[rb] = bump ? exp2_fast(ws.m[rb] - mnew) : 1.f;  // m = -inf -> 0
+    ws.m[rb] = mnew;
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void softmax_p(const float (&x)[RB][4], const WaveState<RB>& ws, float (&lsum)[RB],
+                                          half4_t (&pb)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float ref = (ws.m[rb] == -INFINITY) ? 0.f : ws.m[rb];
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[rb][i] - ref);
+    lsum[rb] = (p[0] + p[1]) + (p[2] + p[3]);
+    pb[rb] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void softmax_pf(const float (&x)[RB][4], const WaveState<RB>& ws, float (&lsum)[RB],
+                                           float (&p)[RB][4]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float ref = (ws.m[rb] == -INFINITY) ? 0.f : ws.m[rb];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[rb][i] = exp2_fast(x[rb][i] - ref);
+    lsum[rb] = (p[rb][0] + p[rb][1]) + (p[rb][2] + p[rb][3]);
+  }
+}
+
+template <int RB>
+__device__ __forceinline__ void rescale_o(WaveState<RB>& ws, const float (&alpha)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) scale_acc(ws.o[rb][j], alpha[rb]);
+}
+
 // ---- FP8 E4M3 steps -------------------------------------------------------
 //
 // E4M3 bytes become fp16 with the packed hardware conversion at scale 1.0:
@@ -248,21 +326,59 @@ __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __re
   softmax_step<RB>(x, ws, p, lane, t0, L, kv, rowbase, R, G);
 }
 
+// The scaled scores of one FP8 step (the matrix ops and block scales of
+// step_scores8, without the softmax), for the pipelined loop.
+template <int RB>
+__device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4* __restrict__ qf, int lane,
+                                             float scale_log2, float (&x)[RB][4]) {
+  u32x4 kc[8];
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk) {
+    kc[2 * bk] = u32x4{e4m3x2_lo(kf.k[bk][0]), e4m3x2_hi(kf.k[bk][0]), e4m3x2_lo(kf.k[bk][1]),
+                       e4m3x2_hi(kf.k[bk][1])};
+    kc[2 * bk + 1] = u32x4{e4m3x2_lo(kf.k[bk][2]), e4m3x2_hi(kf.k[bk][2]), e4m3x2_lo(kf.k[bk][3]),
+                           e4m3x2_hi(kf.k[bk][3])};
+  }
+  float fk[4][4];  // [token i][block]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * scale_log2;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    int qo = rb * 8 * kWave + lane;
+    asm volatile("" : "+v"(qo));
+    u32x4 qv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[rb][i] = 0.f;
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_16x16x32(kc[2 * bk], qv[2 * bk], acc);
+      acc = mfma_16x16x32(kc[2 * bk + 1], qv[2 * bk + 1], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[rb][i] += fk[i][bk] * acc[i];
+    }
+  }
+}
+
 // O^T += V^T . P^T for one FP8 step: MFMA block j = 4*bb + c holds channels
 // 64*bb + 4*(lane%16) + c, all inside scale block bb, so the V scale is folded
 // into P^T once per block group and V is used exactly.
-template <int RB>
-__device__ __forceinline__ void step_pv8(VFrag8& vf, const KFrag8& kf, const float (&p)[RB][4],
+template <int RB, bool MASK = true>
+__device__ __forceinline__ void step_pv8(VFrag8& vf, const u32x4 (&sv)[2], const float (&p)[RB][4],
                                          WaveState<RB>& ws, int lane, int t0, int kv) {
   const int hi = lane >> 4;
   float fv[4][4];  // [token i][block]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) fv[i][bb] = half_at(kf.sv, 4 * i + bb);
+    for (int bb = 0; bb < 4; ++bb) fv[i][bb] = half_at(sv, 4 * i + bb);
   // Keys at or past kv_len: weight 0; their (poison) scales must not enter
   // and their bytes may decode to NaN (0 * NaN is NaN), so clear both.
-  if (t0 + kStep > kv) {
+  if (MASK && t0 + kStep > kv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (t0 + 4 * hi + i >= kv) {
@@ -297,13 +413,13 @@ __device__ __forceinline__ void step_pv8(VFrag8& vf, const KFrag8& kf, const flo
 }
 
 // O^T += V^T . P^T for one step.
-template <int RB>
+template <int RB, bool MASK = true>
 __device__ __forceinline__ void step_pv(VFrag& vf, const half4_t (&pb)[RB], WaveState<RB>& ws,
                                         int lane, int t0, int kv) {
   const int hi = lane >> 4;
   // Keys at or past kv_len may be poison in the page's unused slots; their
   // weight is exactly 0 but 0 * NaN is NaN, so clear those V rows.
-  if (t0 + kStep > kv) {
+  if (MASK && t0 + kStep > kv) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (t0 + 4 * hi + e >= kv) {
@@ -409,6 +525,27 @@ __device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) 
   for (int j = B0; j < B1; ++j)
     __builtin_amdgcn_global_load_lds(SV_GP(vb + (j * kWave + lane) * 8), SV_LP(ring + j * 1024), 16, 0, 0);
 }
+// The same read into accumulation registers: for fragments that only feed
+// matrix ops (which read A/B operands from them), keeping them out of the
+// ordinary register file.
+template <int VMCNT, int STRIDE>
+__device__ __forceinline__ void ring_read8_acc(u32x4 (&d)[8], uint32_t addr) {
+  asm volatile(
+      "s_waitcnt vmcnt(%9)\n\t"
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&a"(d[0]), "=&a"(d[1]), "=&a"(d[2]), "=&a"(d[3]), "=&a"(d[4]), "=&a"(d[5]), "=&a"(d[6]), "=&a"(d[7])
+      : "v"(addr), "n"(VMCNT), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE), "n"(4 * STRIDE),
+        "n"(5 * STRIDE), "n"(6 * STRIDE), "n"(7 * STRIDE)
+      : "memory");
+}
 // Per-lane ring offsets of the operand reads. K: lane (token l%16, group
 // l/16) reads k-step s at k_lane_off + 64*s. V: fragment 2e+h (token
 // 4*(l/16)+e, channels 128h + 8*(l%16)) at v_lane_off + 256*(2e+h).
@@ -500,26 +637,54 @@ __device__ __forceinline__ void ring_read_v8(VFrag8& f, uint32_t addr) {
       : "memory");
 }
 
-constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
-// A wave keeps one step in flight in its private ring (64 KB per CU over the
-// four waves): that saturates HBM for this access pattern, and on MI355X a
-// second step in flight per wave measured slower, not faster.
+template <int RB>
+__device__ __forceinline__ void scores_mfma(const KFrag& kf, const u32x4* __restrict__ qf, int lane,
+                                            float scale_log2, float (&x)[RB][4]) {
+  const uint32_t q_lds = lds_addr(qf);
+  floatx4 acc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // the row block's 8 Q fragments (1 KB apart in LDS) with one wait, then
+    // two independent chains of four (even and odd k-steps)
+    u32x4 qv[8];
+    ring_read8<63, false, 1024>(qv, q_lds + (uint32_t)(rb * 8 * kWave + lane) * 16u);
+    floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      a0 = mfma_16x16x32(kf.k[s], qv[s], a0);
+      a1 = mfma_16x16x32(kf.k[s + 1], qv[s + 1], a1);
+    }
+    acc[rb] = a0 + a1;
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[rb][i] = acc[rb][i] * scale_log2;
+}
 
-template <int RB, bool FP8>
+constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
+// DEPTH steps in flight per wave in its private ring. One (64 KB per CU over
+// the four waves) saturates HBM when every workgroup streams its own keys; a
+// second step measured slower there. When two workgroups read the same keys
+// (more than 48 rows per KV head) they share one HBM stream, and two steps
+// each keep as many HBM bytes in flight as one step does unshared.
+
+template <int RB, bool FP8, int DEPTH>
 struct Smem {
   static constexpr int QBYTES = RB * 8 * kWave * 16;
   static constexpr int OBYTES = RB * 16 * kRowStride * 4;
-  // a private one-step ring per wave
-  static constexpr int RBYTES = kWavesPerGroup * (FP8 ? kStage8 : kRingStage);
+  // a private DEPTH-step ring per wave
+  static constexpr int RBYTES = kWavesPerGroup * DEPTH * (FP8 ? kStage8 : kRingStage);
   // Q fragments in their own array (so reading them never waits for the
   // ring's DMAs); the ring and, after the main loop, the combine buffer
   // share the second array.
   static constexpr int BIG = RBYTES > OBYTES ? RBYTES : OBYTES;
 };
 
-template <int RB, bool FP8>
+template <int RB, bool FP8, int DEPTH>
 __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
-  using SM = Smem<RB, FP8>;
+  static_assert(DEPTH == 1 || DEPTH == 2, "one or two steps in flight");
+  using SM = Smem<RB, FP8, DEPTH>;
   constexpr int NTS = kWavesPerGroup;  // waves that split the chunk's steps
   __shared__ __attribute__((aligned(1024))) unsigned char qsm[SM::QBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char bigsm[SM::BIG];
@@ -603,19 +768,26 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     const int pg = __builtin_amdgcn_readlane(pid, kk);
     return ((size_t)pg * Hkv + g) * P + ((chunk_lo + kStep * (ts + (bstart + kk) * NTS)) % P);
   };
-  char* const ring = reinterpret_cast<char*>(bigsm) + wave * (FP8 ? kStage8 : kRingStage);
-  // The first step's DMAs go out before Q is staged, so the two latencies
-  // overlap (Q lives in its own array; the ring is the wave's own).
+  constexpr int kStageBytes = FP8 ? kStage8 : kRingStage;
+  char* const ring = reinterpret_cast<char*>(bigsm) + wave * DEPTH * kStageBytes;
+  // The first steps' DMAs go out before Q is staged, so the two latencies
+  // overlap (Q lives in its own array; the ring is the wave's own). Step
+  // indices past the batch are clamped to its last step.
   int pid_first = 0;
   if (my_steps > 0) {
     pid_first = page_ids(0);
-    const size_t tr = tok_row(pid_first, 0, 0);
-    if constexpr (FP8) {
-      dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring, lane);
-      dma_v8(vpool8 + tr * kHeadDim, ring, lane);
-    } else {
-      dma_k<0, 8>(kpool + tr * kHeadDim, ring, lane);
-      dma_v<0, 8>(vpool + tr * kHeadDim, ring + 8192, lane);
+    const int nb0 = min(kWave, my_steps);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const size_t tr = tok_row(pid_first, 0, min(d, nb0 - 1));
+      char* stage = ring + d * kStageBytes;
+      if constexpr (FP8) {
+        dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, stage, lane);
+        dma_v8(vpool8 + tr * kHeadDim, stage, lane);
+      } else {
+        dma_k<0, 8>(kpool + tr * kHeadDim, stage, lane);
+        dma_v<0, 8>(vpool + tr * kHeadDim, stage + 8192, lane);
+      }
     }
   }
 
@@ -650,6 +822,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const u32x4* qf = qlds;
   const int rowbase = 0;               // first row of the wave, local to the workgroup
   const int growbase = row0 + rowbase;  // the same row in the KV head's numbering
+  // visible-key limit (exclusive) of each of this lane's rows (row r sees
+  // cache positions < L + r/G + 1; padding rows see every key)
+  int rowlim[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = growbase + rb * 16 + (lane & 15);
+    rowlim[rb] = r < R ? min(L + r / G + 1, kv) : kv;
+  }
   if constexpr (FP8) {
     // ---- FP8: each wave owns its token steps and a private one-step ring ----
     // (same schedule as the fp16 ring below; half-steps are K bytes + both
@@ -667,23 +847,60 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       auto issue_v = [&](int kk, int stg) {
         dma_v8(vpool8 + tok_row(pid, bstart, kk) * kHeadDim, ring + stg * kStage8, lane);
       };
-      if (bstart > 0) {  // (the first batch's first step was issued before Q staging)
-        issue_k(0, 0);
-        issue_v(0, 0);
+      if (bstart > 0) {  // (the first batch's first steps were issued before Q staging)
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          issue_k(min(d, nb - 1), d);
+          issue_v(min(d, nb - 1), d);
+        }
       }
-      for (int kk = 0; kk < nb; ++kk) {
-        const int t0 = step_t0(kk);
-        const int kn = min(kk + 1, nb - 1);
-        const uint32_t sbase = ring_lds;
+      // before a K read the newer operations are V(k) and, with two steps
+      // in flight, K(k+1), V(k+1): 4 or 13; before a V read K(k+1) and, with
+      // two, V(k+1), K(k+2): 5 or 14
+      constexpr int kWaitK = DEPTH == 1 ? 4 : 13, kWaitV = DEPTH == 1 ? 5 : 14;
+      // Software pipeline as in the fp16 loop: step k's PV runs while step
+      // k+1's softmax is computed (same read order, so the same waits).
+      auto sbase = [&](int kk) { return ring_lds + (kk & (DEPTH - 1)) * kStage8; };
+      float pr[RB][4];
+      u32x4 sv[2];  // V scales of the step whose PV is next
+      {
         KFrag8 kf;
-        ring_read_k8<4>(kf, sbase + k8_lane_off(lane), sbase + 8192 + 32 * (lane >> 4));
-        issue_k(kn, 0);
-        float pr[RB][4];
-        step_scores8<RB>(kf, qf, ws, pr, lane, t0, L, kv, growbase, R, G, a.scale_log2);
+        ring_read_k8<kWaitK>(kf, sbase(0) + k8_lane_off(lane), sbase(0) + 8192 + 32 * (lane >> 4));
+        issue_k(min(DEPTH, nb - 1), 0);
+        step_scores8<RB>(kf, qf, ws, pr, lane, step_t0(0), L, kv, growbase, R, G, a.scale_log2);
+        sv[0] = kf.sv[0];
+        sv[1] = kf.sv[1];
+      }
+      for (int kk = 0; kk + 1 < nb; ++kk) {
+        const int t0 = step_t0(kk);
         VFrag8 vf;
-        ring_read_v8<5>(vf, sbase + 4096 + v8_lane_off(lane));
-        issue_v(kn, 0);
-        step_pv8<RB>(vf, kf, pr, ws, lane, t0, kv);
+        ring_read_v8<kWaitV>(vf, sbase(kk) + 4096 + v8_lane_off(lane));
+        issue_v(min(kk + DEPTH, nb - 1), kk & (DEPTH - 1));
+        KFrag8 kf;
+        ring_read_k8<kWaitK>(kf, sbase(kk + 1) + k8_lane_off(lane), sbase(kk + 1) + 8192 + 32 * (lane >> 4));
+        issue_k(min(kk + 1 + DEPTH, nb - 1), (kk + 1) & (DEPTH - 1));
+        float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
+        scores8_mfma<RB>(kf, qf, lane, a.scale_log2, x);
+        // (a step before the wave's last of the batch ends below kv_len)
+        step_pv8<RB, false>(vf, sv, pr, ws, lane, t0, kv);
+        sv[0] = kf.sv[0];
+        sv[1] = kf.sv[1];
+        const bool any = mask_check<RB>(x, lmx, ws, rowlim, lane, step_t0(kk + 1));
+        softmax_pf<RB>(x, ws, lsum, pr);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
+        if (any) {
+          move_ref<RB>(lmx, ws, alpha);
+          softmax_pf<RB>(x, ws, lsum, pr);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) ws.l[rb] = ws.l[rb] * alpha[rb] + lsum[rb];
+        if (any) rescale_o<RB>(ws, alpha);
+      }
+      {
+        VFrag8 vf;
+        ring_read_v8<kWaitV>(vf, sbase(nb - 1) + 4096 + v8_lane_off(lane));
+        step_pv8<RB>(vf, sv, pr, ws, lane, step_t0(nb - 1), kv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -694,29 +911,62 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       const int nb = min(kWave, my_steps - bstart);
       auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
       auto step_base = [&](int kk, const _Float16* pool) { return pool + tok_row(pid, bstart, kk) * kHeadDim; };
-      // One step in flight per wave in its ring, one in registers. Order of
-      // DMA issue: K(k+1) right after K(k) is read, V(k+1) right after V(k)
-      // is read, so before reading a half-step exactly the other half-step
-      // (8 operations) is newer. The index past the batch is clamped to its
-      // last step (a duplicate request that hits in cache) to keep that
-      // count exact.
+      // DEPTH steps in flight per wave in its ring, one in registers. Order
+      // of DMA issue: K(k+DEPTH) right after K(k) is read, V(k+DEPTH) right
+      // after V(k) is read, so before reading a half-step exactly 2*DEPTH-1
+      // newer half-steps (8 operations each) may be outstanding. Indices
+      // past the batch are clamped to its last step (a duplicate request
+      // that hits in cache) to keep that count exact.
       const uint32_t ring_lds = lds_addr(ring);
-      if (bstart > 0) {  // (the first batch's first step was issued before Q staging)
-        dma_k<0, 8>(step_base(0, kpool), ring, lane);
-        dma_v<0, 8>(step_base(0, vpool), ring + 8192, lane);
+      if (bstart > 0) {  // (the first batch's first steps were issued before Q staging)
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          const int kd = min(d, nb - 1);
+          dma_k<0, 8>(step_base(kd, kpool), ring + d * kRingStage, lane);
+          dma_v<0, 8>(step_base(kd, vpool), ring + d * kRingStage + 8192, lane);
+        }
       }
-      for (int kk = 0; kk < nb; ++kk) {
-        const int t0 = step_t0(kk);
-        const int kn = min(kk + 1, nb - 1);
+      constexpr int kWait = 8 * (2 * DEPTH - 1);
+      auto stage = [&](int kk) { return (kk & (DEPTH - 1)) * kRingStage; };
+      // Software pipeline: step k's PV runs while step k+1's softmax is
+      // computed. Read order K(0), V(0), K(1), V(1), ... and the DMA after
+      // each read are those of the plain loop, so the waits are the same.
+      half4_t pb[RB];
+      {
         KFrag kf;
-        ring_read8<8, false, 64>(kf.k, ring_lds + k_lane_off(lane));
-        dma_k<0, 8>(step_base(kn, kpool), ring, lane);
-        half4_t pb[RB];
-        step_scores<RB>(kf, qf, ws, pb, lane, t0, L, kv, growbase, R, G, a.scale_log2);
+        ring_read8<kWait, false, 64>(kf.k, ring_lds + stage(0) + k_lane_off(lane));
+        dma_k<0, 8>(step_base(min(DEPTH, nb - 1), kpool), ring + stage(0), lane);
+        step_scores<RB>(kf, qf, ws, pb, lane, step_t0(0), L, kv, growbase, R, G, a.scale_log2);
+      }
+      for (int kk = 0; kk + 1 < nb; ++kk) {
+        const int t0 = step_t0(kk);
+        const int st = stage(kk), st1 = stage(kk + 1);
         VFrag vf;
-        ring_read8<8, false, 256>(vf.v, ring_lds + 8192 + v_lane_off(lane));
-        dma_v<0, 8>(step_base(kn, vpool), ring + 8192, lane);
-        step_pv<RB>(vf, pb, ws, lane, t0, kv);
+        ring_read8<kWait, false, 256>(vf.v, ring_lds + st + 8192 + v_lane_off(lane));
+        dma_v<0, 8>(step_base(min(kk + DEPTH, nb - 1), vpool), ring + st + 8192, lane);
+        KFrag kf;
+        ring_read8_acc<kWait, 64>(kf.k, ring_lds + st1 + k_lane_off(lane));
+        dma_k<0, 8>(step_base(min(kk + 1 + DEPTH, nb - 1), kpool), ring + st1, lane);
+        float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
+        scores_mfma<RB>(kf, qf, lane, a.scale_log2, x);
+        // (a step before the wave's last of the batch ends below kv_len)
+        step_pv<RB, false>(vf, pb, ws, lane, t0, kv);
+        const bool any = mask_check<RB>(x, lmx, ws, rowlim, lane, step_t0(kk + 1));
+        softmax_p<RB>(x, ws, lsum, pb);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
+        if (any) {
+          move_ref<RB>(lmx, ws, alpha);
+          softmax_p<RB>(x, ws, lsum, pb);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) ws.l[rb] = ws.l[rb] * alpha[rb] + lsum[rb];
+        if (any) rescale_o<RB>(ws, alpha);
+      }
+      {
+        VFrag vf;
+        ring_read8<kWait, false, 256>(vf.v, ring_lds + stage(nb - 1) + 8192 + v_lane_off(lane));
+        step_pv<RB>(vf, pb, ws, lane, step_t0(nb - 1), kv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -845,14 +1095,25 @@ void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s)
   // one workgroup per unit; with two row blocks, 16 ids per 8 units
   const int n = a.row_blocks == 2 ? 2 * ((a.units + 7) / 8 * 8) : a.units;
   dim3 grid(n), block(kThreads);
+  // two workgroups on the same keys (rb is then 2 or 3): two steps in flight
+  if (a.row_blocks == 2) {
+    if (fp8) {
+      if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, true, 2>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((verify_attn_kernel<3, true, 2>), grid, block, 0, s, a);
+    } else {
+      if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false, 2>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((verify_attn_kernel<3, false, 2>), grid, block, 0, s, a);
+    }
+    return;
+  }
   if (fp8) {
-    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, true>), grid, block, 0, s, a);
-    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((verify_attn_kernel<3, true>), grid, block, 0, s, a);
+    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, true, 1>), grid, block, 0, s, a);
+    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, true, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_attn_kernel<3, true, 1>), grid, block, 0, s, a);
   } else {
-    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false>), grid, block, 0, s, a);
-    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((verify_attn_kernel<3, false>), grid, block, 0, s, a);
+    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false, 1>), grid, block, 0, s, a);
+    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((verify_attn_kernel<3, false, 1>), grid, block, 0, s, a);
   }
 }
 
