@@ -326,44 +326,6 @@ __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __re
   softmax_step<RB>(x, ws, p, lane, t0, L, kv, rowbase, R, G);
 }
 
-// The scaled scores of one FP8 step (the matrix ops and block scales of
-// step_scores8, without the softmax), for the pipelined loop.
-template <int RB>
-__device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4* __restrict__ qf, int lane,
-                                             float scale_log2, float (&x)[RB][4]) {
-  u32x4 kc[8];
-#pragma unroll
-  for (int bk = 0; bk < 4; ++bk) {
-    kc[2 * bk] = u32x4{e4m3x2_lo(kf.k[bk][0]), e4m3x2_hi(kf.k[bk][0]), e4m3x2_lo(kf.k[bk][1]),
-                       e4m3x2_hi(kf.k[bk][1])};
-    kc[2 * bk + 1] = u32x4{e4m3x2_lo(kf.k[bk][2]), e4m3x2_hi(kf.k[bk][2]), e4m3x2_lo(kf.k[bk][3]),
-                           e4m3x2_hi(kf.k[bk][3])};
-  }
-  float fk[4][4];  // [token i][block]
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * scale_log2;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    int qo = rb * 8 * kWave + lane;
-    asm volatile("" : "+v"(qo));
-    u32x4 qv[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[rb][i] = 0.f;
-#pragma unroll
-    for (int bk = 0; bk < 4; ++bk) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_16x16x32(kc[2 * bk], qv[2 * bk], acc);
-      acc = mfma_16x16x32(kc[2 * bk + 1], qv[2 * bk + 1], acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[rb][i] += fk[i][bk] * acc[i];
-    }
-  }
-}
-
 // O^T += V^T . P^T for one FP8 step: MFMA block j = 4*bb + c holds channels
 // 64*bb + 4*(lane%16) + c, all inside scale block bb, so the V scale is folded
 // into P^T once per block group and V is used exactly.
@@ -660,6 +622,46 @@ __device__ __forceinline__ void scores_mfma(const KFrag& kf, const u32x4* __rest
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[rb][i] = acc[rb][i] * scale_log2;
+}
+
+// The scaled scores of one FP8 step (the matrix ops and block scales of
+// step_scores8, without the softmax), for the pipelined loop: Q read with
+// one wait per row block, one accumulator per (row block, scale block) so
+// the block scales are applied after all matrix ops are issued.
+template <int RB>
+__device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4* __restrict__ qf, int lane,
+                                             float scale_log2, float (&x)[RB][4]) {
+  u32x4 kc[8];
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk) {
+    kc[2 * bk] = u32x4{e4m3x2_lo(kf.k[bk][0]), e4m3x2_hi(kf.k[bk][0]), e4m3x2_lo(kf.k[bk][1]),
+                       e4m3x2_hi(kf.k[bk][1])};
+    kc[2 * bk + 1] = u32x4{e4m3x2_lo(kf.k[bk][2]), e4m3x2_hi(kf.k[bk][2]), e4m3x2_lo(kf.k[bk][3]),
+                           e4m3x2_hi(kf.k[bk][3])};
+  }
+  const uint32_t q_lds = lds_addr(qf);
+  floatx4 acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    u32x4 qv[8];
+    ring_read8<63, false, 1024>(qv, q_lds + (uint32_t)(rb * 8 * kWave + lane) * 16u);
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      acc[rb][bk] = mfma_16x16x32(kc[2 * bk], qv[2 * bk], floatx4{0.f, 0.f, 0.f, 0.f});
+      acc[rb][bk] = mfma_16x16x32(kc[2 * bk + 1], qv[2 * bk + 1], acc[rb][bk]);
+    }
+  }
+  float fk[4][4];  // [token i][block]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * scale_log2;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[rb][i] = (fk[i][0] * acc[rb][0][i] + fk[i][1] * acc[rb][1][i]) +
+                 (fk[i][2] * acc[rb][2][i] + fk[i][3] * acc[rb][3][i]);
 }
 
 constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
