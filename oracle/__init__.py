@@ -13,6 +13,9 @@ from the pages' definitions:
     widths);
   * ``block.prepare_block`` / ``block.append_kv`` — a block's packed rows,
     positions and cache slots, and writing its K/V into the reserved slots;
+  * ``sampling.rejection_accept``  — stochastic acceptance: drafts kept by
+    rejection sampling against target and draft probabilities, the final
+    draw from the residual (or the last row);
   * ``fp8.e4m3_decode``            — the OCP E4M3 value of each byte;
   * ``brute``                      — pure-Python loop versions for tiny inputs.
 
