@@ -5,7 +5,7 @@ One step = one verify of a block: paged causal GQA over the long cache
 greedy acceptance over the block's fp32 logits (sv_greedy_accept), on seeded
 synthetic inputs already resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal] [--ragged]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal] [--ragged] [--stochastic]
 
 Prints one JSON line. `value` is the effective HBM bandwidth of the whole step
 (algorithmic bytes of attention + accept / step time). The `roofline` object
@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--ragged", action="store_true",
                     help="also time one round of blocks of a seeded width per request (2..q_len): block "
                          "preparation, K/V append, ragged verify attention and ragged greedy accept")
+    ap.add_argument("--stochastic", action="store_true",
+                    help="also time stochastic acceptance (rejection sampling) on the workload's logits with "
+                         "seeded draft distributions")
     ap.add_argument("--traffic", default=None,
                     help="JSON with measured HBM bytes per verify_attn launch (default: the one under "
                          "profiles/ for this workload, used only while the kernel source is unchanged)")
@@ -233,6 +236,20 @@ def main():
     if args.ragged:
         ragged = ragged_round(x, wl, acc_in, page_table, stream, timed, n_part)
 
+    stoch = None
+    if args.stochastic:
+        si = W.make_sampling_inputs(wl, device=dev)
+        rc = B.RejectionAcceptCall(acc_in.logits, si.draft_ids, si.draft_probs, wl.q_len, 1.0, si.u_accept,
+                                   si.u_final, kv_lens)
+        for _ in range(3):
+            rc.run(stream)
+        us = float(np.median(timed(lambda: rc.run(stream), n_part)))
+        sb = W.rejection_accept_bytes(wl.batch, wl.q_len, wl.vocab)
+        stoch = {"us_median": round(us, 2), "algorithmic_bytes": sb, "GBps": round(sb / (us * 1e-6) / 1e9, 1),
+                 "accept_len": rc.accept_len.cpu().tolist()[:8], "temperature": 1.0}
+        log(f"[bench] rejection accept: {us:.2f} us, {sb / (us * 1e-6) / 1e9:.1f} GB/s")
+        del si, rc
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wl)
@@ -290,6 +307,7 @@ def main():
         "verify_attention_cold": cold,
         "reference_copy": ref_copy,
         "ragged_round": ragged,
+        "rejection_accept": stoch,
     }
     print(json.dumps(res), flush=True)
 

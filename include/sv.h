@@ -1,8 +1,9 @@
 /*
  * sv.h — C ABI of the target-verify path of speculative decoding on MI355X
  * (gfx950): paged causal grouped-query attention of a verify block, the
- * merge of split-KV partials, and greedy acceptance; blocks of one width or
- * of a width per request, and the preparation and K/V append of a block.
+ * merge of split-KV partials, greedy and stochastic (rejection-sampling)
+ * acceptance; blocks of one width or of a width per request, and the
+ * preparation and K/V append of a block.
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless marked "host".
@@ -275,6 +276,44 @@ sv_status sv_append_kv(const void* new_k, const void* new_v, const int32_t* cach
                        int32_t batch, int32_t max_rows, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                        int32_t num_pages, sv_kv_dtype kv_dtype, void* k_pages, void* v_pages,
                        int32_t* status_flags, void* stream);
+
+/* Bytes of workspace sv_rejection_accept needs. */
+size_t sv_rejection_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vocab);
+
+/*
+ * Stochastic acceptance of a verify block: rejection sampling against the
+ * target's and the draft's probabilities (the sampling case of "Why the
+ * target output stayed the same", page "MTP and DFlash2 at long context on
+ * XPU"; a verify post-processing step in section 1.1 of the page "DFlash ->
+ * dLLM self-spec, part 1"). With p_j = softmax(logits row b*q_len + j / T):
+ *     draft d_{j+1} = draft_ids[b][j] is kept while
+ *         u_accept[b][j] * draft_probs[b][j][d] < p_j(d)    (j = 0, 1, ..)
+ *     accept_len[b] = A, the number kept
+ *     token_ids[b]  = the inverse-CDF draw with u_final[b] (the smallest v
+ *         whose cumulative weight exceeds u_final * total weight) from
+ *         max(p_A - draft_probs[b][A], 0) when A < q_len-1 (from p_A if that
+ *         residual is zero everywhere), else from p_{q_len-1}
+ *     kv_lens_out[b] = kv_lens_in[b] - q_len + 1 + A
+ *
+ *   logits       [batch*q_len, vocab] fp32, finite
+ *   draft_ids    [batch, q_len-1] int32 (an id outside 0..vocab-1 is never kept)
+ *   draft_probs  [batch, q_len-1, vocab] fp32: row j is the distribution
+ *                d_{j+1} was drawn from
+ *   temperature  > 0 (the logits are divided by it; no top-k/top-p filter)
+ *   u_accept     [batch, q_len-1] fp32 uniforms on [0, 1); u_final [batch]
+ *                (the caller's random numbers: the call itself is
+ *                deterministic)
+ *   accept_len, token_ids [batch] int32 (written)
+ *   kv_lens_in, kv_lens_out  both NULL, or both [batch] int32 (may alias)
+ *   workspace    sv_rejection_accept_workspace_bytes() bytes, 256-byte aligned
+ * Arithmetic is fp32; q_len <= 64; batch * q_len <= 65535. The three NULL
+ * draft pointers are allowed when q_len == 1.
+ */
+sv_status sv_rejection_accept(const float* logits, const int32_t* draft_ids, const float* draft_probs,
+                              int32_t batch, int32_t q_len, int32_t vocab, float temperature, const float* u_accept,
+                              const float* u_final, int32_t* accept_len, int32_t* token_ids,
+                              const int32_t* kv_lens_in, int32_t* kv_lens_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 const char* sv_status_string(sv_status s);
 const char* sv_last_error(void);

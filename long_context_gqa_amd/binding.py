@@ -24,8 +24,8 @@ SV_FLAG_BAD_BLOCK_WIDTH = 8
 EXPORTED = (
     "sv_verify_workspace_bytes", "sv_verify_plan", "sv_verify_attention", "sv_verify_merge",
     "sv_greedy_accept_workspace_bytes", "sv_greedy_accept", "sv_verify_attention_ragged",
-    "sv_greedy_accept_ragged", "sv_prepare_block", "sv_append_kv", "sv_status_string", "sv_last_error",
-    "sv_version",
+    "sv_greedy_accept_ragged", "sv_prepare_block", "sv_append_kv", "sv_rejection_accept_workspace_bytes",
+    "sv_rejection_accept", "sv_status_string", "sv_last_error", "sv_version",
 )
 
 
@@ -84,6 +84,11 @@ def lib() -> ctypes.CDLL:
         L.sv_prepare_block.restype = ctypes.c_int
         L.sv_append_kv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp]
         L.sv_append_kv.restype = ctypes.c_int
+        L.sv_rejection_accept_workspace_bytes.argtypes = [i32, i32, i32]
+        L.sv_rejection_accept_workspace_bytes.restype = sz
+        L.sv_rejection_accept.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz,
+                                          vp]
+        L.sv_rejection_accept.restype = ctypes.c_int
         L.sv_status_string.argtypes = [ctypes.c_int]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_last_error.argtypes = []
@@ -198,6 +203,19 @@ def sv_append_kv(new_k, new_v, cache_slot, q_start, batch, max_rows, k_pages, v_
     _check(lib().sv_append_kv(_ptr(new_k), _ptr(new_v), _ptr(cache_slot), _ptr(q_start), batch, max_rows, Hkv, D, P,
                               num_pages, SV_KV_FP16 if k_pages.dtype == torch.float16 else SV_KV_FP8_E4M3,
                               _ptr(k_pages), _ptr(v_pages), _ptr(status_flags), _stream(stream)))
+
+
+def sv_rejection_accept_workspace_bytes(batch: int, q_len: int, vocab: int) -> int:
+    return int(lib().sv_rejection_accept_workspace_bytes(batch, q_len, vocab))
+
+
+def sv_rejection_accept(logits, draft_ids, draft_probs, batch, q_len, vocab, temperature, u_accept, u_final,
+                        accept_len, token_ids, kv_lens_in=None, kv_lens_out=None, workspace=None, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sv_rejection_accept(_ptr(logits), _ptr(draft_ids), _ptr(draft_probs), batch, q_len, vocab,
+                                     float(temperature), _ptr(u_accept), _ptr(u_final), _ptr(accept_len),
+                                     _ptr(token_ids), _ptr(kv_lens_in), _ptr(kv_lens_out), _ptr(workspace), ws_bytes,
+                                     _stream(stream)))
 
 
 def sv_version() -> int:
@@ -347,3 +365,27 @@ class PrepareCall:
         sv_prepare_block(*self.args, self.q_start, self.cache_slot, self.positions, self.kv_lens_out,
                          self.last_tokens, self.draft_ids, self.block_ids, self.flags, stream)
         return self
+
+
+class RejectionAcceptCall:
+    """Buffers of one stochastic-acceptance call (rejection sampling); the
+    uniforms are the caller's."""
+
+    def __init__(self, logits, draft_ids, draft_probs, q_len, temperature, u_accept, u_final, kv_lens=None):
+        dev = logits.device
+        self.batch = logits.shape[0] // q_len
+        self.q_len, self.vocab, self.temperature = q_len, logits.shape[1], temperature
+        self.inputs = (logits, draft_ids, draft_probs)
+        self.u_accept, self.u_final = u_accept, u_final
+        self.accept_len = torch.empty(self.batch, dtype=torch.int32, device=dev)
+        self.token = torch.empty(self.batch, dtype=torch.int32, device=dev)
+        self.kv_in = kv_lens
+        self.kv_out = torch.empty_like(kv_lens) if kv_lens is not None else None
+        nbytes = sv_rejection_accept_workspace_bytes(self.batch, q_len, self.vocab)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def run(self, stream=None):
+        lg, ids, dp = self.inputs
+        sv_rejection_accept(lg, ids, dp, self.batch, self.q_len, self.vocab, self.temperature, self.u_accept,
+                            self.u_final, self.accept_len, self.token, self.kv_in, self.kv_out, self.workspace, stream)
+        return self.accept_len, self.token, self.kv_out

@@ -1,0 +1,300 @@
+// Stochastic acceptance of a verify block by rejection sampling: draft
+// d_{j+1} is kept while u_j * q_j(d) < p_j(d), with p_j = softmax(row j / T);
+// the final token is drawn by inverse CDF with u_final from the residual
+// max(p_A - q_A, 0) of the first rejected row A (or from p_{q-1} when every
+// draft is kept).
+//
+// Stage 1 (row_stats): one workgroup per (row, slice of 8,192 columns): the
+//   slice's max of z = logit * log2(e)/T and sum of 2^(z - max), combined
+//   across threads, waves and (in stage 2) slices. One HBM pass over the
+//   logits.
+// Stage 2 (walk_residual): one workgroup per (slice, request): the row
+//   statistics of the request's rows, the acceptance walk (a few element
+//   reads), then the sum over this slice of the weight the final draw uses.
+// Stage 3 (draw): one workgroup per request: the slice where the cumulative
+//   weight passes u_final * total, then a scan inside that slice.
+#include <stdint.h>
+
+#include "sv_common.h"
+#include "sv_sampling.h"
+
+namespace sv {
+
+namespace {
+
+struct Stat {
+  float m, s;  // max of z; sum of 2^(z - m)
+};
+
+__device__ __forceinline__ Stat combine(Stat a, Stat b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -INFINITY) return Stat{-INFINITY, 0.f};
+  return Stat{m, a.s * __builtin_amdgcn_exp2f(a.m - m) + b.s * __builtin_amdgcn_exp2f(b.m - m)};
+}
+
+__device__ __forceinline__ Stat wave_stat(Stat x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Stat y{__shfl_xor(x.m, o), __shfl_xor(x.s, o)};
+    x = combine(x, y);
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Statistics (M, 1/S) of row r from its slices' (m, s).
+__device__ __forceinline__ void row_stat(const float2* __restrict__ ws1, int n_slices, size_t row, float* M,
+                                         float* invS) {
+  Stat t{-INFINITY, 0.f};
+  for (int k = 0; k < n_slices; ++k) {
+    const float2 v = ws1[row * n_slices + k];
+    t = combine(t, Stat{v.x, v.y});
+  }
+  *M = t.m;
+  *invS = t.s > 0.f ? 1.f / t.s : 0.f;
+}
+
+}  // namespace
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void row_stats_kernel(const float* __restrict__ logits, int vocab,
+                                                             int slice, int n_slices, float c, float2* ws1) {
+  const int sl = blockIdx.x, row = blockIdx.y;
+  const int lo = sl * slice, hi = min(lo + slice, vocab);
+  const float* rp = logits + (size_t)row * vocab;
+  Stat st{-INFINITY, 0.f};
+  if (VEC4) {
+    constexpr int kPer = kSampleSlice / (4 * kThreads);
+    float4 v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int col = lo + 4 * (threadIdx.x + u * kThreads);
+      v[u] = col < hi ? *reinterpret_cast<const float4*>(rp + col)
+                      : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) m = fmaxf(m, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)) * c);
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        s += (__builtin_amdgcn_exp2f(v[u].x * c - m) + __builtin_amdgcn_exp2f(v[u].y * c - m)) +
+             (__builtin_amdgcn_exp2f(v[u].z * c - m) + __builtin_amdgcn_exp2f(v[u].w * c - m));
+    }
+    st = Stat{m, s};
+  } else {
+    float m = -INFINITY;
+    for (int col = lo + threadIdx.x; col < hi; col += kThreads) m = fmaxf(m, rp[col] * c);
+    float s = 0.f;
+    if (m != -INFINITY)
+      for (int col = lo + threadIdx.x; col < hi; col += kThreads) s += __builtin_amdgcn_exp2f(rp[col] * c - m);
+    st = Stat{m, s};
+  }
+  st = wave_stat(st);
+  __shared__ Stat sb[kWavesPerGroup];
+  const int w = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) sb[w] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Stat r = sb[0];
+    for (int k = 1; k < kWavesPerGroup; ++k) r = combine(r, sb[k]);
+    ws1[(size_t)row * n_slices + sl] = make_float2(r.m, r.s);
+  }
+}
+
+// Whether draft j of request b passes its test u_j * q_j(d) < p_j(d) (an id
+// outside the vocabulary never does).
+__device__ __forceinline__ bool keeps(const SampleLaunch& a, int b, int j, float M, float invS) {
+  const size_t row = (size_t)b * a.q_len + j;
+  const int d = a.draft_ids[(size_t)b * (a.q_len - 1) + j];
+  if (d < 0 || d >= a.vocab) return false;
+  const float p = __builtin_amdgcn_exp2f(a.logits[row * a.vocab + d] * a.c - M) * invS;
+  const float qd = a.draft_probs[((size_t)b * (a.q_len - 1) + j) * a.vocab + d];
+  return a.u_accept[(size_t)b * (a.q_len - 1) + j] * qd < p;
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void walk_residual_kernel(SampleLaunch a) {
+  const int sl = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ float M[kMaxSampleRows], invS[kMaxSampleRows];
+  __shared__ int keep[kMaxSampleRows];
+  __shared__ int s_acc;
+  // every row's statistics and every draft's test in parallel; the walk
+  // then stops at the first draft that fails (the same in every workgroup)
+  for (int j = tid; j < a.q_len; j += kThreads) {
+    float m, is;
+    row_stat(a.ws1, a.n_slices, (size_t)b * a.q_len + j, &m, &is);
+    M[j] = m;
+    invS[j] = is;
+    keep[j] = (j < a.q_len - 1) ? (int)keeps(a, b, j, m, is) : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    while (acc < a.q_len - 1 && keep[acc]) ++acc;
+    s_acc = acc;
+  }
+  __syncthreads();
+  const int A = s_acc;
+  const bool residual = A < a.q_len - 1;
+  const size_t row = (size_t)b * a.q_len + A;
+  const float* lp = a.logits + row * a.vocab;
+  const float* qp = residual ? a.draft_probs + ((size_t)b * (a.q_len - 1) + A) * a.vocab : nullptr;
+  const float Mr = M[A], iS = invS[A];
+  const int lo = sl * a.slice, hi = min(lo + a.slice, a.vocab);
+  float sum = 0.f;
+  if (VEC4) {
+    for (int col = lo + 4 * tid; col < hi; col += 4 * kThreads) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lp + col);
+      float4 p4 = make_float4(__builtin_amdgcn_exp2f(l4.x * a.c - Mr) * iS, __builtin_amdgcn_exp2f(l4.y * a.c - Mr) * iS,
+                              __builtin_amdgcn_exp2f(l4.z * a.c - Mr) * iS, __builtin_amdgcn_exp2f(l4.w * a.c - Mr) * iS);
+      if (residual) {
+        const float4 q4 = *reinterpret_cast<const float4*>(qp + col);
+        p4 = make_float4(fmaxf(p4.x - q4.x, 0.f), fmaxf(p4.y - q4.y, 0.f), fmaxf(p4.z - q4.z, 0.f),
+                         fmaxf(p4.w - q4.w, 0.f));
+      }
+      sum += (p4.x + p4.y) + (p4.z + p4.w);
+    }
+  } else {
+    for (int col = lo + tid; col < hi; col += kThreads) {
+      float p = __builtin_amdgcn_exp2f(lp[col] * a.c - Mr) * iS;
+      if (residual) p = fmaxf(p - qp[col], 0.f);
+      sum += p;
+    }
+  }
+  sum = wave_sum_f(sum);
+  __shared__ float red[kWavesPerGroup];
+  if (tid % kWave == 0) red[tid / kWave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int k = 0; k < kWavesPerGroup; ++k) t += red[k];
+    a.ws2[(size_t)b * a.n_slices + sl] = t;
+    if (sl == 0) a.ws_acc[b] = A;
+  }
+}
+
+// Weight of column col of request b's chosen row (residual or p).
+__device__ __forceinline__ float weight(const float* lp, const float* qp, float c, float Mr, float iS, int col) {
+  float p = __builtin_amdgcn_exp2f(lp[col] * c - Mr) * iS;
+  if (qp) p = fmaxf(p - qp[col], 0.f);
+  return p;
+}
+
+__global__ __launch_bounds__(kThreads) void draw_kernel(SampleLaunch a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ int s_k, s_mode, s_best, s_last;
+  __shared__ float s_base, s_target, s_M, s_iS;
+  __shared__ float scan[kThreads];
+  const int A = a.ws_acc[b];
+  const bool residual = A < a.q_len - 1;
+  const size_t row = (size_t)b * a.q_len + A;
+  if (tid == 0) {
+    row_stat(a.ws1, a.n_slices, row, &s_M, &s_iS);
+    // totals of the residual's slices; a residual that is zero everywhere
+    // (p = q on that row) falls back to p
+    float tot = 0.f;
+    for (int k = 0; k < a.n_slices; ++k) tot += a.ws2[(size_t)b * a.n_slices + k];
+    int mode = residual ? 1 : 0;
+    if (residual && !(tot > 0.f)) mode = 0;
+    if (mode == 0 && residual) {
+      // p's slice sums from the row statistics
+      tot = 0.f;
+      for (int k = 0; k < a.n_slices; ++k) {
+        const float2 v = a.ws1[row * a.n_slices + k];
+        tot += v.y * __builtin_amdgcn_exp2f(v.x - s_M) * s_iS;
+      }
+    }
+    const float target = a.u_final[b] * tot;
+    float cum = 0.f;
+    int k = -1, last = 0;
+    for (int j = 0; j < a.n_slices; ++j) {
+      float sj;
+      if (mode == 1 || !residual) sj = a.ws2[(size_t)b * a.n_slices + j];
+      else {
+        const float2 v = a.ws1[row * a.n_slices + j];
+        sj = v.y * __builtin_amdgcn_exp2f(v.x - s_M) * s_iS;
+      }
+      if (sj > 0.f) last = j;
+      if (k < 0 && cum + sj > target) {
+        k = j;
+        break;
+      }
+      cum += sj;
+    }
+    s_last = (k < 0) ? 1 : 0;  // rounding put the target past the total: take the last positive weight
+    s_k = (k < 0) ? last : k;
+    s_base = cum;
+    s_target = target;
+    s_mode = mode;
+    s_best = INT32_MAX;
+  }
+  __syncthreads();
+  const float* lp = a.logits + row * a.vocab;
+  const float* qp = s_mode == 1 ? a.draft_probs + ((size_t)b * (a.q_len - 1) + A) * a.vocab : nullptr;
+  const int lo = s_k * a.slice, hi = min(lo + a.slice, a.vocab);
+  const int per = a.slice / kThreads;  // consecutive columns per thread
+  const int c0 = lo + tid * per;
+  float loc = 0.f;
+  for (int i = 0; i < per; ++i)
+    if (c0 + i < hi) loc += weight(lp, qp, a.c, s_M, s_iS, c0 + i);
+  scan[tid] = loc;
+  __syncthreads();
+  // inclusive scan of the threads' sums (fixed order)
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const float v = tid >= o ? scan[tid - o] : 0.f;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const float excl = s_base + (scan[tid] - loc);
+  if (!s_last) {
+    if (excl + loc > s_target) {  // the crossing is in this thread's columns
+      float run = excl;
+      for (int i = 0; i < per; ++i) {
+        if (c0 + i >= hi) break;
+        run += weight(lp, qp, a.c, s_M, s_iS, c0 + i);
+        if (run > s_target) {
+          atomicMin(&s_best, c0 + i);
+          break;
+        }
+      }
+    }
+  } else {
+    int mine = -1;
+    for (int i = 0; i < per; ++i)
+      if (c0 + i < hi && weight(lp, qp, a.c, s_M, s_iS, c0 + i) > 0.f) mine = c0 + i;
+    if (mine >= 0) atomicMin(&s_best, -mine);  // the largest index, as a minimum of negatives
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int tok = s_best;
+    if (s_last) tok = (tok == INT32_MAX) ? hi - 1 : -tok;
+    if (tok == INT32_MAX) tok = hi - 1;  // (cannot happen when the slice was chosen by its sum)
+    a.accept_len[b] = A;
+    a.token_ids[b] = tok;
+    if (a.kv_lens_out) a.kv_lens_out[b] = a.kv_lens_in[b] - a.q_len + 1 + A;
+  }
+}
+
+void launch_rejection_accept(const SampleLaunch& a, hipStream_t s) {
+  dim3 g1(a.n_slices, a.batch * a.q_len), g2(a.n_slices, a.batch);
+  if (a.vocab % 4 == 0) {
+    hipLaunchKernelGGL((row_stats_kernel<true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.slice, a.n_slices,
+                       a.c, a.ws1);
+    hipLaunchKernelGGL((walk_residual_kernel<true>), g2, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((row_stats_kernel<false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.slice, a.n_slices,
+                       a.c, a.ws1);
+    hipLaunchKernelGGL((walk_residual_kernel<false>), g2, dim3(kThreads), 0, s, a);
+  }
+  hipLaunchKernelGGL(draw_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
+}
+
+}  // namespace sv

@@ -11,6 +11,7 @@
 #include "sv_accept.h"
 #include "sv_block.h"
 #include "sv_common.h"
+#include "sv_sampling.h"
 
 namespace {
 
@@ -466,6 +467,63 @@ sv_status sv_append_kv(const void* new_k, const void* new_v, const int32_t* cach
   a.num_pages = num_pages;
   sv::launch_append_kv(a, static_cast<hipStream_t>(stream));
   return check_launch("append_kv");
+}
+
+size_t sv_rejection_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vocab) {
+  if (batch < 1 || q_len < 1 || vocab < 1) return 0;
+  const size_t slices = ((size_t)vocab + sv::kSampleSlice - 1) / sv::kSampleSlice;
+  return align256((size_t)batch * q_len * slices * sizeof(float2)) + align256((size_t)batch * slices * sizeof(float)) +
+         align256((size_t)batch * sizeof(int32_t));
+}
+
+sv_status sv_rejection_accept(const float* logits, const int32_t* draft_ids, const float* draft_probs,
+                              int32_t batch, int32_t q_len, int32_t vocab, float temperature, const float* u_accept,
+                              const float* u_final, int32_t* accept_len, int32_t* token_ids,
+                              const int32_t* kv_lens_in, int32_t* kv_lens_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (batch < 1 || q_len < 1 || vocab < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "batch, q_len and vocab must be >= 1");
+  if (q_len > sv::kMaxSampleRows) return fail(SV_ERR_UNSUPPORTED, "q_len must be <= %d", sv::kMaxSampleRows);
+  if ((long long)batch * q_len > 65535) return fail(SV_ERR_UNSUPPORTED, "batch * q_len must be <= 65535");
+  if (!(temperature > 0.f) || temperature > 1e30f)
+    return fail(SV_ERR_INVALID_ARGUMENT, "temperature must be positive and finite");
+  if (!logits || !u_final || !accept_len || !token_ids)
+    return fail(SV_ERR_INVALID_ARGUMENT, "logits, u_final, accept_len and token_ids must be non-NULL");
+  if (q_len > 1 && (!draft_ids || !draft_probs || !u_accept))
+    return fail(SV_ERR_INVALID_ARGUMENT, "draft_ids, draft_probs and u_accept must be non-NULL when q_len > 1");
+  if ((kv_lens_in == nullptr) != (kv_lens_out == nullptr))
+    return fail(SV_ERR_INVALID_ARGUMENT, "kv_lens_in and kv_lens_out must be both NULL or both set");
+  if (vocab % 4 == 0 && ((reinterpret_cast<uintptr_t>(logits) | reinterpret_cast<uintptr_t>(draft_probs)) % 16))
+    return fail(SV_ERR_INVALID_ARGUMENT, "logits and draft_probs must be 16-byte aligned");
+  const size_t need = sv_rejection_accept_workspace_bytes(batch, q_len, vocab);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(SV_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  sv::SampleLaunch a;
+  a.logits = logits;
+  a.draft_ids = draft_ids;
+  a.draft_probs = draft_probs;
+  a.u_accept = u_accept;
+  a.u_final = u_final;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.vocab = vocab;
+  a.slice = sv::kSampleSlice;
+  a.n_slices = (vocab + sv::kSampleSlice - 1) / sv::kSampleSlice;
+  a.c = 1.44269504088896340736f / temperature;
+  a.accept_len = accept_len;
+  a.token_ids = token_ids;
+  a.kv_lens_in = kv_lens_in;
+  a.kv_lens_out = kv_lens_out;
+  char* w = static_cast<char*>(workspace);
+  a.ws1 = reinterpret_cast<float2*>(w);
+  w += align256((size_t)batch * q_len * a.n_slices * sizeof(float2));
+  a.ws2 = reinterpret_cast<float*>(w);
+  w += align256((size_t)batch * a.n_slices * sizeof(float));
+  a.ws_acc = reinterpret_cast<int32_t*>(w);
+  sv::launch_rejection_accept(a, static_cast<hipStream_t>(stream));
+  return check_launch("rejection_accept");
 }
 
 const char* sv_status_string(sv_status s) {

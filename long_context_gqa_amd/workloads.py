@@ -96,7 +96,7 @@ def _seed(base: int, stream: int, chunk: int = 0) -> int:
     return (base * 1_000_003 + stream * 10_007 + chunk * 7_919 + 12_345) & ((1 << 63) - 1)
 
 
-S_PREFIX, S_PAGES, S_Q, S_K, S_V, S_BIAS, S_LOGITS, S_ACCEPT, S_DRAFT, S_WIDTH = range(10)
+S_PREFIX, S_PAGES, S_Q, S_K, S_V, S_BIAS, S_LOGITS, S_ACCEPT, S_DRAFT, S_WIDTH, S_SAMPLE = range(11)
 
 
 def _gen(device, base, stream, chunk=0):
@@ -365,6 +365,36 @@ def make_accept_inputs(wl: Workload, device="cpu", planted: list[int] | None = N
     logits[rows, targets.flatten().to(device)] = 8.0
     return AcceptInputs(logits, drafts.to(torch.int32).to(device),
                         torch.tensor(planted, dtype=torch.int32), targets.to(torch.int32))
+
+
+@dataclass
+class SamplingInputs:
+    draft_probs: torch.Tensor  # fp32 [B, q-1, V]: each row a distribution
+    draft_ids: torch.Tensor    # int32 [B, q-1], drawn from draft_probs
+    u_accept: torch.Tensor     # fp32 [B, q-1] uniforms on [0, 1)
+    u_final: torch.Tensor      # fp32 [B]
+
+
+def make_sampling_inputs(wl: Workload, device="cpu") -> SamplingInputs:
+    """The draft side of a stochastic verify: a distribution per draft
+    position (normalised exponential draws, i.e. Dirichlet(1) over the
+    vocabulary), the draft tokens drawn from them, and the uniforms of the
+    acceptance tests and of the final draw. Random numbers only."""
+    B, q, V = wl.batch, wl.q_len, wl.vocab
+    g = _gen(torch.device(device).type, wl.seed, S_SAMPLE)
+    e = torch.empty((B, max(q - 1, 0), V), dtype=torch.float32, device=device).exponential_(generator=g)
+    probs = e / e.sum(dim=-1, keepdim=True)
+    ids = torch.multinomial(probs.view(-1, V), 1, generator=g).view(B, max(q - 1, 0)).to(torch.int32) \
+        if q > 1 else torch.zeros((B, 0), dtype=torch.int32, device=device)
+    ua = torch.rand((B, max(q - 1, 0)), generator=g, device=device)
+    uf = torch.rand((B,), generator=g, device=device)
+    return SamplingInputs(probs.contiguous(), ids.contiguous(), ua.contiguous(), uf.contiguous())
+
+
+def rejection_accept_bytes(batch, q_len, vocab) -> int:
+    """Target logits read once, the draft distribution of the first rejected
+    row, the tested draft elements, uniforms and outputs."""
+    return batch * q_len * vocab * 4 + batch * vocab * 4 + batch * max(q_len - 1, 0) * (4 + 4 + 4) + 4 * batch * 4
 
 
 # ---------------------------------------------------------------------------

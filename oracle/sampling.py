@@ -61,11 +61,11 @@ def rejection_accept(logits, draft_ids, draft_probs, q_len, temperature, u_accep
     and u_final [B] uniforms on [0, 1).
     """
     logits = _np(logits)
-    ids = _np(draft_ids, np.int64).reshape(-1, max(q_len - 1, 0))
-    dq = _np(draft_probs, np.float64)
-    ua = _np(u_accept, np.float64).reshape(-1, max(q_len - 1, 0))
-    uf = _np(u_final, np.float64)
     B = logits.shape[0] // q_len
+    ids = _np(draft_ids, np.int64).reshape(B, q_len - 1)
+    dq = _np(draft_probs, np.float64)
+    ua = _np(u_accept, np.float64).reshape(B, q_len - 1)
+    uf = _np(u_final, np.float64)
     acc = np.zeros(B, dtype=np.int64)
     tok = np.zeros(B, dtype=np.int64)
     for b in range(B):

@@ -161,3 +161,27 @@ def test_block_entry_points_reject_bad_arguments_without_launch():
     assert st == B.SV_ERR_INVALID_ARGUMENT  # misaligned
     st = lib.sv_append_kv(None, fake, fake, fake, 2, 16, 4, 256, 16, 100, B.SV_KV_FP16, fake, fake, None, None)
     assert st == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_rejection_accept_rejects_bad_arguments_without_launch():
+    lib = B.lib()
+    fake = 1 << 40
+    need = lib.sv_rejection_accept_workspace_bytes(4, 8, 248320)
+    assert need == 4 * 8 * 31 * 8 + ((4 * 31 * 4 + 255) // 256) * 256 + 256
+    ok = [fake, fake, fake, 4, 8, 248320, 1.0, fake, fake, fake, fake, None, None, fake, need, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["logits", "ids", "probs", "batch", "q", "vocab", "T", "ua", "uf", "acc", "tok", "kin", "kout",
+                 "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.sv_rejection_accept(*args)
+
+    assert call(T=0.0) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(T=float("nan")) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(q=65) == B.SV_ERR_UNSUPPORTED
+    assert call(probs=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(kin=fake) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(wsb=need - 1) == B.SV_ERR_WORKSPACE_TOO_SMALL
+    assert call(logits=fake + 4) == B.SV_ERR_INVALID_ARGUMENT

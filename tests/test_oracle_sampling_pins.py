@@ -134,3 +134,16 @@ def test_impossible_draft_is_rejected_and_never_redrawn():
         for uf in (0.01, 0.5, 0.99):
             acc, tok, _ = osm.rejection_accept(logits, ids, dq, q_len, T, np.array([[u, u]]), np.array([uf]))
             assert acc[0] == 1 and tok[0] != 4
+
+
+def test_no_drafts_is_a_plain_draw_from_row_zero():
+    rng = np.random.default_rng(5)
+    B, V, T = 4, 30, 0.7
+    logits = rng.standard_normal((B, V))
+    uf = rng.random(B)
+    acc, tok, new = osm.rejection_accept(logits, np.zeros((B, 0), int), np.zeros((B, 0, V)), 1, T,
+                                         np.zeros((B, 0)), uf, np.full(B, 9))
+    np.testing.assert_array_equal(acc, 0)
+    np.testing.assert_array_equal(new, 9)  # kv_len - 1 + 1 + 0: the drawn token is not cached yet
+    for b in range(B):
+        assert tok[b] == osm.inverse_cdf(softmax(logits[b] / T), uf[b])
