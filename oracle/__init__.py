@@ -16,6 +16,8 @@ from the pages' definitions:
   * ``sampling.rejection_accept``  — stochastic acceptance: drafts kept by
     rejection sampling against target and draft probabilities, the final
     draw from the residual (or the last row);
+  * ``topk.topk``                  — the k highest candidate logits of each row
+    (value descending, lower index first on ties);
   * ``fp8.e4m3_decode``            — the OCP E4M3 value of each byte;
   * ``brute``                      — pure-Python loop versions for tiny inputs.
 
