@@ -5,7 +5,7 @@ One step = one verify of a block: paged causal GQA over the long cache
 greedy acceptance over the block's fp32 logits (sv_greedy_accept), on seeded
 synthetic inputs already resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal] [--ragged] [--stochastic]
+    python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal] [--ragged] [--stochastic] [--topk]
 
 Prints one JSON line. `value` is the effective HBM bandwidth of the whole step
 (algorithmic bytes of attention + accept / step time). The `roofline` object
@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--stochastic", action="store_true",
                     help="also time stochastic acceptance (rejection sampling) on the workload's logits with "
                          "seeded draft distributions")
+    ap.add_argument("--topk", action="store_true",
+                    help="also time top-16 candidate selection over the workload's logits")
     ap.add_argument("--traffic", default=None,
                     help="JSON with measured HBM bytes per verify_attn launch (default: the one under "
                          "profiles/ for this workload, used only while the kernel source is unchanged)")
@@ -250,6 +252,19 @@ def main():
         log(f"[bench] rejection accept: {us:.2f} us, {sb / (us * 1e-6) / 1e9:.1f} GB/s")
         del si, rc
 
+    topk = None
+    if args.topk:
+        tc = B.TopkCall(acc_in.logits, 16)
+        for _ in range(3):
+            tc.run(stream)
+        us = float(np.median(timed(lambda: tc.run(stream), n_part)))
+        rows_k = acc_in.logits.shape[0]
+        tb = rows_k * wl.vocab * 4 + rows_k * 16 * 8
+        topk = {"rows": rows_k, "k": 16, "us_median": round(us, 2), "algorithmic_bytes": tb,
+                "GBps": round(tb / (us * 1e-6) / 1e9, 1)}
+        log(f"[bench] top-16 over {rows_k} rows: {us:.2f} us, {tb / (us * 1e-6) / 1e9:.1f} GB/s")
+        del tc
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wl)
@@ -308,6 +323,7 @@ def main():
         "reference_copy": ref_copy,
         "ragged_round": ragged,
         "rejection_accept": stoch,
+        "topk_candidates": topk,
     }
     print(json.dumps(res), flush=True)
 

@@ -2,8 +2,8 @@
  * sv.h — C ABI of the target-verify path of speculative decoding on MI355X
  * (gfx950): paged causal grouped-query attention of a verify block, the
  * merge of split-KV partials, greedy and stochastic (rejection-sampling)
- * acceptance; blocks of one width or of a width per request, and the
- * preparation and K/V append of a block.
+ * acceptance, top-k candidate selection; blocks of one width or of a width
+ * per request, and the preparation and K/V append of a block.
  *
  * Conventions shared by every entry point
  *   - Pointers are DEVICE pointers unless marked "host".
@@ -314,6 +314,30 @@ sv_status sv_rejection_accept(const float* logits, const int32_t* draft_ids, con
                               const float* u_final, int32_t* accept_len, int32_t* token_ids,
                               const int32_t* kv_lens_in, int32_t* kv_lens_out, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace sv_topk_candidates needs. */
+size_t sv_topk_candidates_workspace_bytes(int32_t rows, int32_t vocab, int32_t k);
+
+/*
+ * Top-k candidate selection over the vocabulary (the draft side's per-position
+ * top-16 candidate sets of DFlash2: page "MTP and DFlash2 at long context on
+ * XPU", the DFlash2 description — a local top 16 per shard, then a top 16 of
+ * the gathered candidates, equal to the unsharded set; the PocketLLM page's
+ * split top-16 with one comparator). For every row:
+ *     out_ids[row][0..k-1] = the k columns with the largest logits, in order:
+ *     larger value first, the lower column index first among equal values
+ *     out_values[row][j]   = logits[row][out_ids[row][j]]
+ *
+ *   logits      [rows, vocab] fp32 (NaN order is unspecified; -inf allowed)
+ *   k           1..16, k <= vocab; vocab <= 512/k * 8192 columns (262,144 at k = 16)
+ *   out_ids     [rows, k] int32 (written); out_values [rows, k] fp32 (written)
+ *   workspace   sv_topk_candidates_workspace_bytes() bytes
+ * rows <= 65535. The same kernels give the top k of any slice union, so a
+ * vocabulary-sharded head can run them per shard and merge the per-shard
+ * lists with this call on the gathered candidates.
+ */
+sv_status sv_topk_candidates(const float* logits, int32_t rows, int32_t vocab, int32_t k, int32_t* out_ids,
+                             float* out_values, void* workspace, size_t workspace_bytes, void* stream);
 
 const char* sv_status_string(sv_status s);
 const char* sv_last_error(void);

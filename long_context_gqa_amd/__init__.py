@@ -6,9 +6,9 @@ include/sv.h); ``binding`` wraps its entry points with ctypes, and
 """
 from . import binding, workloads  # noqa: F401
 from .binding import (  # noqa: F401
-    AcceptCall, PrepareCall, RaggedAcceptCall, RaggedVerifyCall, RejectionAcceptCall, SvError, VerifyCall, greedy_accept,
+    AcceptCall, PrepareCall, RaggedAcceptCall, RaggedVerifyCall, RejectionAcceptCall, SvError, TopkCall, VerifyCall, greedy_accept,
     make_params, sv_append_kv, sv_greedy_accept, sv_greedy_accept_ragged, sv_greedy_accept_workspace_bytes,
-    sv_prepare_block, sv_rejection_accept, sv_verify_attention, sv_verify_attention_ragged, sv_verify_merge,
+    sv_prepare_block, sv_rejection_accept, sv_topk_candidates, sv_verify_attention, sv_verify_attention_ragged, sv_verify_merge,
     sv_verify_plan,
     sv_verify_workspace_bytes, verify_attention,
 )

@@ -25,7 +25,8 @@ EXPORTED = (
     "sv_verify_workspace_bytes", "sv_verify_plan", "sv_verify_attention", "sv_verify_merge",
     "sv_greedy_accept_workspace_bytes", "sv_greedy_accept", "sv_verify_attention_ragged",
     "sv_greedy_accept_ragged", "sv_prepare_block", "sv_append_kv", "sv_rejection_accept_workspace_bytes",
-    "sv_rejection_accept", "sv_status_string", "sv_last_error", "sv_version",
+    "sv_rejection_accept", "sv_topk_candidates_workspace_bytes", "sv_topk_candidates", "sv_status_string",
+    "sv_last_error", "sv_version",
 )
 
 
@@ -89,6 +90,10 @@ def lib() -> ctypes.CDLL:
         L.sv_rejection_accept.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz,
                                           vp]
         L.sv_rejection_accept.restype = ctypes.c_int
+        L.sv_topk_candidates_workspace_bytes.argtypes = [i32, i32, i32]
+        L.sv_topk_candidates_workspace_bytes.restype = sz
+        L.sv_topk_candidates.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.sv_topk_candidates.restype = ctypes.c_int
         L.sv_status_string.argtypes = [ctypes.c_int]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_last_error.argtypes = []
@@ -216,6 +221,17 @@ def sv_rejection_accept(logits, draft_ids, draft_probs, batch, q_len, vocab, tem
                                      float(temperature), _ptr(u_accept), _ptr(u_final), _ptr(accept_len),
                                      _ptr(token_ids), _ptr(kv_lens_in), _ptr(kv_lens_out), _ptr(workspace), ws_bytes,
                                      _stream(stream)))
+
+
+def sv_topk_candidates_workspace_bytes(rows: int, vocab: int, k: int) -> int:
+    return int(lib().sv_topk_candidates_workspace_bytes(rows, vocab, k))
+
+
+def sv_topk_candidates(logits, k, out_ids, out_values, workspace, stream=None):
+    rows, vocab = logits.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().sv_topk_candidates(_ptr(logits), rows, vocab, k, _ptr(out_ids), _ptr(out_values), _ptr(workspace),
+                                    ws_bytes, _stream(stream)))
 
 
 def sv_version() -> int:
@@ -389,3 +405,20 @@ class RejectionAcceptCall:
         sv_rejection_accept(lg, ids, dp, self.batch, self.q_len, self.vocab, self.temperature, self.u_accept,
                             self.u_final, self.accept_len, self.token, self.kv_in, self.kv_out, self.workspace, stream)
         return self.accept_len, self.token, self.kv_out
+
+
+class TopkCall:
+    """Buffers of one top-k candidate call over logits [rows, vocab]."""
+
+    def __init__(self, logits, k=16):
+        dev = logits.device
+        rows, vocab = logits.shape
+        self.logits, self.k = logits, k
+        self.ids = torch.empty((rows, k), dtype=torch.int32, device=dev)
+        self.values = torch.empty((rows, k), dtype=torch.float32, device=dev)
+        nbytes = sv_topk_candidates_workspace_bytes(rows, vocab, k)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def run(self, stream=None):
+        sv_topk_candidates(self.logits, self.k, self.ids, self.values, self.workspace, stream)
+        return self.ids, self.values

@@ -12,6 +12,7 @@
 #include "sv_block.h"
 #include "sv_common.h"
 #include "sv_sampling.h"
+#include "sv_topk.h"
 
 namespace {
 
@@ -524,6 +525,43 @@ sv_status sv_rejection_accept(const float* logits, const int32_t* draft_ids, con
   a.ws_acc = reinterpret_cast<int32_t*>(w);
   sv::launch_rejection_accept(a, static_cast<hipStream_t>(stream));
   return check_launch("rejection_accept");
+}
+
+size_t sv_topk_candidates_workspace_bytes(int32_t rows, int32_t vocab, int32_t k) {
+  if (rows < 1 || vocab < 1 || k < 1) return 0;
+  const size_t slices = ((size_t)vocab + sv::kTopkSlice - 1) / sv::kTopkSlice;
+  return align256((size_t)rows * slices * k * sizeof(float2));
+}
+
+sv_status sv_topk_candidates(const float* logits, int32_t rows, int32_t vocab, int32_t k, int32_t* out_ids,
+                             float* out_values, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 1 || vocab < 1) return fail(SV_ERR_INVALID_ARGUMENT, "rows and vocab must be >= 1");
+  if (k < 1 || k > sv::kMaxTopk) return fail(SV_ERR_UNSUPPORTED, "k must be in 1..%d (got %d)", sv::kMaxTopk, k);
+  if (k > vocab) return fail(SV_ERR_INVALID_ARGUMENT, "k (%d) exceeds vocab (%d)", k, vocab);
+  if (rows > 65535) return fail(SV_ERR_UNSUPPORTED, "rows must be <= 65535");
+  const long long slices = ((long long)vocab + sv::kTopkSlice - 1) / sv::kTopkSlice;
+  if (slices * k > (long long)sv::kWave * sv::kMergePerLane)
+    return fail(SV_ERR_UNSUPPORTED, "vocab too large for k = %d (at most %d columns)", k,
+                sv::kWave * sv::kMergePerLane / k * sv::kTopkSlice);
+  if (!logits || !out_ids || !out_values)
+    return fail(SV_ERR_INVALID_ARGUMENT, "logits, out_ids and out_values must be non-NULL");
+  if (vocab % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16)
+    return fail(SV_ERR_INVALID_ARGUMENT, "logits must be 16-byte aligned");
+  const size_t need = sv_topk_candidates_workspace_bytes(rows, vocab, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  sv::TopkLaunch a;
+  a.logits = logits;
+  a.rows = rows;
+  a.vocab = vocab;
+  a.k = k;
+  a.n_slices = (int)slices;
+  a.ws = static_cast<float2*>(workspace);
+  a.out_ids = out_ids;
+  a.out_vals = out_values;
+  sv::launch_topk(a, static_cast<hipStream_t>(stream));
+  return check_launch("topk_candidates");
 }
 
 const char* sv_status_string(sv_status s) {

@@ -185,3 +185,16 @@ def test_rejection_accept_rejects_bad_arguments_without_launch():
     assert call(kin=fake) == B.SV_ERR_INVALID_ARGUMENT
     assert call(wsb=need - 1) == B.SV_ERR_WORKSPACE_TOO_SMALL
     assert call(logits=fake + 4) == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_topk_rejects_bad_arguments_without_launch():
+    lib = B.lib()
+    fake = 1 << 40
+    need = lib.sv_topk_candidates_workspace_bytes(8, 248320, 16)
+    assert need == 8 * 31 * 16 * 8
+    assert lib.sv_topk_candidates(fake, 8, 248320, 17, fake, fake, fake, need, None) == B.SV_ERR_UNSUPPORTED
+    assert lib.sv_topk_candidates(fake, 8, 248320, 0, fake, fake, fake, need, None) == B.SV_ERR_UNSUPPORTED
+    assert lib.sv_topk_candidates(fake, 8, 10, 11, fake, fake, fake, need, None) == B.SV_ERR_INVALID_ARGUMENT
+    assert lib.sv_topk_candidates(fake, 8, 1 << 20, 16, fake, fake, fake, 1 << 30, None) == B.SV_ERR_UNSUPPORTED
+    assert lib.sv_topk_candidates(fake, 8, 248320, 16, fake, fake, fake, need - 1, None) == B.SV_ERR_WORKSPACE_TOO_SMALL
+    assert lib.sv_topk_candidates(None, 8, 248320, 16, fake, fake, fake, need, None) == B.SV_ERR_INVALID_ARGUMENT
