@@ -8,6 +8,8 @@ from the pages' definitions:
   * ``attention.merge_partials``   — combining split-KV partials (o, lse);
   * ``attention.verify_attention_ragged`` — the same with a different block
     width per request (rows packed request by request);
+  * ``attention.verify_attention_window`` — the same over a leading sink
+    prefix plus a sliding window of the newest positions;
   * ``accept.greedy_accept``       — argmax per row, longest matching draft
     prefix, bonus token, new cache length (``greedy_accept_ragged``: per-request
     widths);

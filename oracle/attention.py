@@ -221,3 +221,54 @@ def verify_attention_ragged(q, k_pages, v_pages, page_table, kv_lens, q_lens, q_
                 out[r, h] = (w @ V[:n]) / l
                 lse[r, h] = m + np.log(l)
     return out, lse
+
+
+def visible_keys(pos, window, sink):
+    """Cache positions a row at position pos attends to with a sliding window
+    of `window` positions (0: no window) and `sink` leading positions: every
+    t <= pos with window == 0, or t < sink, or t > pos - window."""
+    t = np.arange(pos + 1)
+    if window == 0:
+        return t
+    return t[(t < sink) | (t > pos - window)]
+
+
+def verify_attention_window(q, k_pages, v_pages, page_table, kv_lens, q_len, sm_scale, window, sink,
+                            k_scales=None, v_scales=None, rows=None):
+    """Verify attention with a leading sink prefix plus a sliding window.
+
+    The PocketLLM page ("Implemented execution path"; "Validated performance",
+    sparse experiments) describes an opt-in sparse mode that attends to the
+    leading `sink` positions plus the newest `window` positions, without
+    changing the KV-cache storage, and `window` = 0 is exact full attention.
+    Reading taken: the window is counted per verify row and includes the row
+    itself, so row i (position p = kv_len - q_len + i) sees t <= p with
+    t < sink or t > p - window. Same layouts and return values as
+    ``verify_attention``.
+    """
+    q = _as_np(q)
+    k_pages, v_pages = _as_np(k_pages), _as_np(v_pages)
+    k_scales, v_scales = _as_np(k_scales), _as_np(v_scales)
+    page_table, kv_lens = _as_np(page_table), _as_np(kv_lens)
+    R, Hq, D = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    B = len(kv_lens)
+    out = np.full((R, Hq, D), np.nan)
+    lse = np.full((R, Hq), np.nan)
+    groups = [(b, g) for b in range(B) for g in range(Hkv)] if rows is None else list(rows)
+    for b, g in groups:
+        n_all = int(kv_lens[b])
+        K = gather_kv(k_pages, k_scales, page_table[b], n_all, g)
+        V = gather_kv(v_pages, v_scales, page_table[b], n_all, g)
+        for i in range(q_len):
+            vis = visible_keys(n_all - q_len + i, window, sink)
+            r = b * q_len + i
+            for h in range(g * G, (g + 1) * G):
+                s = sm_scale * (K[vis] @ q[r, h].astype(np.float64))
+                m = s.max()
+                w = np.exp(s - m)
+                l = w.sum()
+                out[r, h] = (w @ V[vis]) / l
+                lse[r, h] = m + np.log(l)
+    return out, lse
