@@ -6,6 +6,7 @@ greedy acceptance over the block's fp32 logits (sv_greedy_accept), on seeded
 synthetic inputs already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal] [--ragged] [--stochastic] [--topk]
+                    [--window W --sink S]
 
 Prints one JSON line. `value` is the effective HBM bandwidth of the whole step
 (algorithmic bytes of attention + accept / step time). The `roofline` object
@@ -61,6 +62,9 @@ def parse():
                          "seeded draft distributions")
     ap.add_argument("--topk", action="store_true",
                     help="also time top-16 candidate selection over the workload's logits")
+    ap.add_argument("--window", type=int, default=0,
+                    help="also time the sink + sliding-window verify with this window (positions)")
+    ap.add_argument("--sink", type=int, default=0, help="leading sink positions for --window")
     ap.add_argument("--traffic", default=None,
                     help="JSON with measured HBM bytes per verify_attn launch (default: the one under "
                          "profiles/ for this workload, used only while the kernel source is unchanged)")
@@ -265,6 +269,26 @@ def main():
         log(f"[bench] top-16 over {rows_k} rows: {us:.2f} us, {tb / (us * 1e-6) / 1e9:.1f} GB/s")
         del tc
 
+    win = None
+    if args.window > 0:
+        wc = B.VerifyCall(x.q, x.k_pages, x.v_pages, page_table, kv_lens, wl.q_len, x.max_kv_len, x.k_scales,
+                          x.v_scales, x.sm_scale, 0, window=args.window, sink=args.sink)
+        for _ in range(3):
+            wc.run(stream)
+        us = float(np.median(timed(lambda: wc.run(stream), n_part)))
+        # keys the block can see: [0, sink) and [L + 1 - window, kv) per request
+        vis = []
+        for n in x.kv_lens.tolist():
+            lo = max(n - wl.q_len + 1 - args.window, 0)
+            vis.append(min(args.sink, lo) + (n - lo))
+        wb = W.verify_algorithmic_bytes(vis, wl.q_len, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size,
+                                        wl.kv_dtype)
+        win = {"window": args.window, "sink": args.sink, "us_median": round(us, 2), "visible_keys": sum(vis),
+               "algorithmic_bytes": wb, "GBps": round(wb / (us * 1e-6) / 1e9, 1), "splits": wc.splits,
+               "chunk_tokens": wc.chunk, "flags": int(wc.flags.item())}
+        log(f"[bench] window {args.window} sink {args.sink}: {us:.2f} us over {sum(vis)} visible keys")
+        del wc
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wl)
@@ -324,6 +348,7 @@ def main():
         "ragged_round": ragged,
         "rejection_accept": stoch,
         "topk_candidates": topk,
+        "window_verify": win,
     }
     print(json.dumps(res), flush=True)
 

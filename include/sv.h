@@ -62,6 +62,13 @@ typedef enum { SV_KV_FP16 = 0, SV_KV_FP8_E4M3 = 1 } sv_kv_dtype;
  * page "DFlash -> dLLM self-spec, part 1"). The block's own K/V are already
  * in the paged cache and kv_lens counts them: row i of request b attends to
  * cache positions 0 .. kv_lens[b] - q_len + i.
+ *
+ * Sink + sliding window (window > 0; the opt-in sparse mode of the PocketLLM
+ * page, "Implemented execution path" and "Validated performance"): row i at
+ * position p = kv_lens[b] - q_len + i attends only to the positions t <= p
+ * with t < sink or t > p - window (the window includes the row itself); the
+ * cache layout is unchanged and chunks the block cannot see are not read.
+ * window = 0 (with sink = 0) is full attention.
  */
 typedef struct {
   int32_t batch;             /* B >= 1 requests */
@@ -76,6 +83,8 @@ typedef struct {
   sv_kv_dtype kv_dtype;
   float sm_scale;            /* softmax scale, e.g. 1/sqrt(D) */
   int32_t num_splits;        /* 0 = automatic; > 0 forces the number of key chunks */
+  int32_t window;            /* 0 = full attention; > 0: a sliding window of this many positions */
+  int32_t sink;              /* with a window: leading positions every row also sees (0 = none) */
 } sv_verify_params;
 
 /*
@@ -87,7 +96,10 @@ size_t sv_verify_workspace_bytes(const sv_verify_params* p);
 /*
  * Number of key chunks (splits) the planner uses for these parameters, and
  * the chunk length in tokens. Chunks are anchored at absolute position 0:
- * chunk s covers cache positions [s*chunk, (s+1)*chunk). Host only.
+ * chunk s covers cache positions [s*chunk, (s+1)*chunk). With a sliding
+ * window the chunks instead tile the positions a block can see (its sink
+ * positions, then its window, in 16-position steps), so the split count
+ * follows sink + window + q_len rather than max_kv_len. Host only.
  */
 sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t* chunk_tokens);
 

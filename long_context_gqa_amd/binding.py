@@ -50,6 +50,8 @@ class SvVerifyParams(ctypes.Structure):
         ("kv_dtype", ctypes.c_int),
         ("sm_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("sink", ctypes.c_int32),
     ]
 
 
@@ -130,11 +132,12 @@ def _check(status: int):
 
 
 def make_params(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                max_pages_per_req, max_kv_len, kv_dtype=SV_KV_FP16, sm_scale=None, num_splits=0):
+                max_pages_per_req, max_kv_len, kv_dtype=SV_KV_FP16, sm_scale=None, num_splits=0, window=0,
+                sink=0):
     if sm_scale is None:
         sm_scale = head_dim ** -0.5
     return SvVerifyParams(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                          max_pages_per_req, max_kv_len, kv_dtype, sm_scale, num_splits)
+                          max_pages_per_req, max_kv_len, kv_dtype, sm_scale, num_splits, window, sink)
 
 
 def sv_verify_workspace_bytes(p: SvVerifyParams) -> int:
@@ -247,14 +250,14 @@ class VerifyCall:
     across launches (the benchmark times ``run`` in a loop)."""
 
     def __init__(self, q, k_pages, v_pages, page_table, kv_lens, q_len, max_kv_len,
-                 k_scales=None, v_scales=None, sm_scale=None, num_splits=0, with_lse=True):
+                 k_scales=None, v_scales=None, sm_scale=None, num_splits=0, with_lse=True, window=0, sink=0):
         dev = q.device
         B = kv_lens.shape[0]
         Hq, D = q.shape[1], q.shape[2]
         Hkv, P = k_pages.shape[1], k_pages.shape[2]
         dtype = SV_KV_FP8_E4M3 if k_pages.dtype == torch.uint8 else SV_KV_FP16
         self.params = make_params(B, q_len, Hq, Hkv, D, P, k_pages.shape[0], page_table.shape[1],
-                                  max_kv_len, dtype, sm_scale, num_splits)
+                                  max_kv_len, dtype, sm_scale, num_splits, window, sink)
         self.inputs = (q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens)
         self.out = torch.empty_like(q)
         self.out_lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=dev) if with_lse else None
@@ -270,12 +273,12 @@ class VerifyCall:
 
 
 def verify_attention(q, k_pages, v_pages, page_table, kv_lens, q_len, max_kv_len=None, k_scales=None,
-                     v_scales=None, sm_scale=None, num_splits=0):
+                     v_scales=None, sm_scale=None, num_splits=0, window=0, sink=0):
     """One verify-attention call; returns (out fp16, lse fp32, status flags)."""
     if max_kv_len is None:
         raise ValueError("max_kv_len (a host upper bound) is required")
     c = VerifyCall(q, k_pages, v_pages, page_table, kv_lens, q_len, max_kv_len, k_scales, v_scales, sm_scale,
-                   num_splits)
+                   num_splits, window=window, sink=sink)
     c.run()
     return c.out, c.out_lse, c.flags
 

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     // chunk was written directly, and chunks past its length hold nothing
     int dummy = 0;
     int b = row / a.q_len;
+    int q_b = a.q_len;
     if (a.q_start) {
       // packed rows: the request is the last b with q_start[b] <= row; rows
       // of no request (past the block, or of a marked request) are skipped
@@ -62,9 +63,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
       int st = 0;
       const int n = block_rows(a.q_start, b, a.batch, a.q_len, &st, &dummy);
       if (row < st || row >= st + n) return;
+      q_b = n;
     }
     const int kv = clamp_kv_len(a.kv_lens[b], a.max_kv_len, a.max_pages, a.page_size, &dummy);
-    const int nch = kv > 0 ? (kv + a.chunk - 1) / a.chunk : 1;
+    // the chunks the attention wrote: the block's live key steps in chunks
+    // of a.chunk / 16 steps (the count the attention kernel uses)
+    int n_sink, w0;
+    const int total = live_steps(kv, kv - q_b, a.window, a.sink, &n_sink, &w0);
+    const int cs = a.chunk / 16;
+    const int nch = total > 0 ? (total + cs - 1) / cs : 1;
     if (nch <= 1) return;
     S = min(S, nch);
   }

@@ -93,6 +93,9 @@ sv_status validate(const sv_verify_params* p) {
   if (!(p->sm_scale > 0.f) || p->sm_scale > 1e6f)
     return fail(SV_ERR_INVALID_ARGUMENT, "sm_scale must be positive and finite");
   if (p->num_splits < 0) return fail(SV_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (p->window < 0 || p->sink < 0) return fail(SV_ERR_INVALID_ARGUMENT, "window and sink must be >= 0");
+  if (p->window == 0 && p->sink != 0)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sink positions need a window (window 0 is full attention)");
   if (p->batch > 65535 || p->num_kv_heads > 65535)
     return fail(SV_ERR_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
   return ok();
@@ -112,7 +115,14 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     pl->row_blocks = 2;
     pl->rb = (rbt + 1) / 2;
   }
-  const long long maxkv = p->max_kv_len;
+  // positions the chunks tile: the whole context, or with a sliding window
+  // at most the sink, the window and the block (plus 16-token alignment)
+  long long maxkv = p->max_kv_len;
+  if (p->window > 0) {
+    const long long live = (long long)p->sink + p->window + p->q_len + 48;
+    const long long whole = (maxkv + 15) / 16 * 16;
+    maxkv = live < whole ? live : whole;
+  }
   const long long rgs = pl->row_blocks;  // workgroups per (chunk, KV head, request)
   long long S;
   if (p->num_splits > 0) {
@@ -229,6 +239,8 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.scale_log2 = p->sm_scale * 1.44269504088896340736f;
   a.row_blocks = pl.row_blocks;
   a.units = pl.splits * p->num_kv_heads * p->batch;
+  a.window = p->window;
+  a.sink = p->sink;
   sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
@@ -241,6 +253,8 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
     m.kv_lens = kv_lens;
     m.q_start = q_start;
     m.batch = p->batch;
+    m.window = p->window;
+    m.sink = p->sink;
     m.num_splits = pl.splits;
     m.num_rows = p->batch * p->q_len;
     m.num_heads = p->num_q_heads;
@@ -299,6 +313,8 @@ sv_status sv_verify_merge(const float* part_o, const float* part_lse, int32_t nu
   m.kv_lens = nullptr;
   m.q_start = nullptr;
   m.batch = 0;
+  m.window = 0;
+  m.sink = 0;
   m.num_splits = num_splits;
   m.num_rows = num_rows;
   m.num_heads = num_heads;

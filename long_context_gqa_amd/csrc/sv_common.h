@@ -37,6 +37,7 @@ struct AttnArgs {
   int32_t num_pages, max_pages, max_kv_len, chunk, num_splits;
   int32_t row_blocks;  // workgroups per (chunk, KV head, request): 1, or 2 for > 48 rows
   int32_t units;       // num_splits * num_kv_heads * batch, numbered split-major
+  int32_t window, sink;  // sliding window (0: full attention) and leading sink positions
   float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -49,6 +50,7 @@ struct MergeArgs {
   const int32_t* q_start;  // optional (with kv_lens): packed row offsets [batch+1]
   int32_t num_splits, num_rows, num_heads, head_dim;
   int32_t q_len, chunk, max_kv_len, max_pages, page_size, batch;
+  int32_t window, sink;  // as in AttnArgs (the chunks tile the block's live key steps)
 };
 
 // Length of request b as the kernels use it: the stored value clamped to the
@@ -79,6 +81,29 @@ __device__ inline int block_rows(const int32_t* q_start, int b, int batch, int m
   }
   *start = s;
   return e - s;
+}
+
+// The 16-token key steps a verify block whose first row is at position L
+// reads from a cache of kv positions. Without a window (window 0): every step
+// from position 0. With a sliding window of `window` positions and `sink`
+// leading positions: the block sees [0, sink) and [L + 1 - window, kv), so
+// the steps are *n_sink from position 0 (the sink part the window does not
+// cover), then steps from *a2 (the window part, from a 16-aligned position).
+// Key chunks tile these steps (chunk s = steps [s*cs, (s+1)*cs)); the
+// attention and merge kernels both count them here.
+__device__ inline int live_steps(int kv, int L, int window, int sink, int* n_sink, int* a2) {
+  *n_sink = 0;
+  *a2 = 0;
+  if (kv <= 0) return 0;
+  if (window == 0) return (kv + 15) / 16;
+  const int wlo = L + 1 - window > 0 ? L + 1 - window : 0;
+  const int s_end = sink < wlo ? sink : wlo;
+  const int ns = (s_end + 15) / 16;
+  int w0 = (wlo / 16) * 16;
+  if (w0 < 16 * ns) w0 = 16 * ns;
+  *n_sink = ns;
+  *a2 = w0;
+  return ns + (kv > w0 ? (kv - w0 + 15) / 16 : 0);
 }
 
 void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s);

@@ -94,27 +94,38 @@ struct WaveState {
   float l[RB];        // this lane's share of the running sum
 };
 
-// Scores of one step, online-softmax update, and the fp16 P^T fragments.
-// Online-softmax update of one step from the scaled scores x (log2 units,
-// lane holds tokens t0 + 4*(lane/16) + i of row lane%16 in each row block):
-// causal/tail masking, the lazy reference, the running sum, and p.
+// The keys each of a lane's rows sees: t < lim (causal and tail limit) and,
+// with a sliding window, t >= lo or t < sink (the leading sink positions).
+// Without a window lo is INT_MIN.
+template <int RB>
+struct RowMask {
+  int lim[RB];
+  int lo[RB];
+  int sink;
+};
+
+// Masking of one step's scores (lane holds tokens t0 + 4*(lane/16) + i of row
+// lane%16 in each row block), without branches.
+template <int RB>
+__device__ __forceinline__ void apply_mask(float (&x)[RB][4], const RowMask<RB>& mk, int lane, int t0) {
+  const int tok = t0 + 4 * (lane >> 4);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tok + i;
+      x[rb][i] = (t >= mk.lim[rb] || (t < mk.lo[rb] && t >= mk.sink)) ? -INFINITY : x[rb][i];
+    }
+}
+
+// Online-softmax update of one step from the scaled scores x (log2 units):
+// masking, the lazy reference, the running sum, and p.
 template <int RB>
 __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& ws, float (&p)[RB][4],
-                                             int lane, int t0, int L, int kv, int rowbase, int R,
-                                             int G) {
-  const int lo = lane & 15, hi = lane >> 4;
-  const bool tail = (t0 + kStep > L + 1);  // some key here is hidden from some row
+                                             int lane, int t0, const RowMask<RB>& mk) {
+  apply_mask<RB>(x, mk, lane, t0);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if (tail) {
-      const int r = rowbase + rb * 16 + lo;
-      int lim = kv;
-      if (r < R) lim = min(L + r / G + 1, kv);
-      const int tok = t0 + 4 * hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (tok + i >= lim) x[rb][i] = -INFINITY;
-    }
     float mx = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -143,8 +154,7 @@ __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& w
 template <int RB>
 __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __restrict__ qf,
                                             WaveState<RB>& ws, half4_t (&pb)[RB], int lane, int t0,
-                                            int L, int kv, int rowbase, int R, int G,
-                                            float scale_log2) {
+                                            const RowMask<RB>& mk, float scale_log2) {
   float x[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -162,7 +172,7 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
     for (int i = 0; i < 4; ++i) x[rb][i] = acc[i] * scale_log2;
   }
   float p[RB][4];
-  softmax_step<RB>(x, ws, p, lane, t0, L, kv, rowbase, R, G);
+  softmax_step<RB>(x, ws, p, lane, t0, mk);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
     pb[rb] = half4_t{(_Float16)p[rb][0], (_Float16)p[rb][1], (_Float16)p[rb][2], (_Float16)p[rb][3]};
@@ -185,13 +195,11 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
 //                 old reference.
 template <int RB>
 __device__ __forceinline__ bool mask_check(float (&x)[RB][4], float (&lmx)[RB], const WaveState<RB>& ws,
-                                           const int (&rowlim)[RB], int lane, int t0) {
-  const int tok = t0 + 4 * (lane >> 4);
+                                           const RowMask<RB>& mk, int lane, int t0) {
+  apply_mask<RB>(x, mk, lane, t0);
   bool bump = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[rb][i] = (tok + i >= rowlim[rb]) ? -INFINITY : x[rb][i];
     lmx[rb] = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
     bump = bump || (lmx[rb] > ws.m[rb] + kLazyLog2);
   }
@@ -289,8 +297,7 @@ __device__ __forceinline__ float half_at(const u32x4 (&h)[2], int idx) {
 template <int RB>
 __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __restrict__ qf,
                                              WaveState<RB>& ws, float (&p)[RB][4], int lane, int t0,
-                                             int L, int kv, int rowbase, int R, int G,
-                                             float scale_log2) {
+                                             const RowMask<RB>& mk, float scale_log2) {
   u32x4 kc[8];
 #pragma unroll
   for (int bk = 0; bk < 4; ++bk) {
@@ -323,7 +330,7 @@ __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __re
       for (int i = 0; i < 4; ++i) x[rb][i] += fk[i][bk] * acc[i];
     }
   }
-  softmax_step<RB>(x, ws, p, lane, t0, L, kv, rowbase, R, G);
+  softmax_step<RB>(x, ws, p, lane, t0, mk);
 }
 
 // O^T += V^T . P^T for one FP8 step: MFMA block j = 4*bb + c holds channels
@@ -735,15 +742,25 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const int raw_kv = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
   const int kv = clamp_kv_len(raw_kv, a.max_kv_len, a.max_pages, a.page_size, &flag_bits);
   if (raw_kv < q_len) flag_bits |= 0x2;
-  const int n_chunks = kv > 0 ? (kv + a.chunk - 1) / a.chunk : 1;
-  const int chunk_lo = split * a.chunk;
-  if (split >= n_chunks) return;  // whole group: nothing of this request here
-  const int chunk_hi = min(chunk_lo + a.chunk, kv);
   const int L = kv - q_len;
+  const int W = a.window, S = a.sink;
+  // Key chunks tile the block's live 16-token steps (all steps from position
+  // 0, or with a sliding window the sink steps then the window steps):
+  // chunk `split` holds steps [split*cs, split*cs + n_steps).
+  int n_sink, w0;
+  const int total = live_steps(kv, L, W, S, &n_sink, &w0);
+  const int cs = a.chunk / kStep;
+  const int n_chunks = total > 0 ? (total + cs - 1) / cs : 1;
+  if (split >= n_chunks) return;  // whole group: nothing of this request here
   const bool direct = (n_chunks == 1);
+  const int k_base = split * cs;
+  const int n_steps = min(total - k_base, cs) > 0 ? min(total - k_base, cs) : 0;
+  auto live_t0 = [&](int j) {
+    const int k = k_base + j;
+    return k < n_sink ? kStep * k : w0 + kStep * (k - n_sink);
+  };
   if (tid == 0) s_flag = 0;
 
-  const int n_steps = (chunk_hi > chunk_lo) ? (chunk_hi - chunk_lo + kStep - 1) / kStep : 0;
   const int my_steps = n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0;
   const int P = a.page_size, Hkv = a.num_kv_heads;
   const _Float16* kpool = static_cast<const _Float16*>(a.k_pages);
@@ -756,7 +773,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     int pid = 0;
     const int kl = bstart + lane;
     if (kl < my_steps) {
-      const int t = chunk_lo + kStep * (ts + kl * NTS);
+      const int t = live_t0(ts + kl * NTS);
       pid = ptab[t / P];
       if (pid < 0 || pid >= a.num_pages) {
         flag_bits |= 0x4;
@@ -768,7 +785,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // (page, KV head, slot) row of the first token of the wave's step bstart + kk
   auto tok_row = [&](int pid, int bstart, int kk) {
     const int pg = __builtin_amdgcn_readlane(pid, kk);
-    return ((size_t)pg * Hkv + g) * P + ((chunk_lo + kStep * (ts + (bstart + kk) * NTS)) % P);
+    return ((size_t)pg * Hkv + g) * P + (live_t0(ts + (bstart + kk) * NTS) % P);
   };
   constexpr int kStageBytes = FP8 ? kStage8 : kRingStage;
   char* const ring = reinterpret_cast<char*>(bigsm) + wave * DEPTH * kStageBytes;
@@ -824,13 +841,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const u32x4* qf = qlds;
   const int rowbase = 0;               // first row of the wave, local to the workgroup
   const int growbase = row0 + rowbase;  // the same row in the KV head's numbering
-  // visible-key limit (exclusive) of each of this lane's rows (row r sees
-  // cache positions < L + r/G + 1; padding rows see every key)
-  int rowlim[RB];
+  // the keys each of this lane's rows sees: row r (block row i = r/G, at
+  // position L + i) sees t <= L + i and, with a window, t > L + i - W or t < S;
+  // padding rows see every key
+  RowMask<RB> mk;
+  mk.sink = S;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = growbase + rb * 16 + (lane & 15);
-    rowlim[rb] = r < R ? min(L + r / G + 1, kv) : kv;
+    mk.lim[rb] = r < R ? min(L + r / G + 1, kv) : kv;
+    mk.lo[rb] = (W > 0 && r < R) ? L + r / G + 1 - W : INT32_MIN;
   }
   if constexpr (FP8) {
     // ---- FP8: each wave owns its token steps and a private one-step ring ----
@@ -841,7 +861,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const int pid = bstart == 0 ? pid_first : page_ids(bstart);
       const int nb = min(kWave, my_steps - bstart);
-      auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
+      auto step_t0 = [&](int kk) { return live_t0(ts + (bstart + kk) * NTS); };
       auto issue_k = [&](int kk, int stg) {
         const size_t tr = tok_row(pid, bstart, kk);
         dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring + stg * kStage8, lane);
@@ -869,7 +889,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         KFrag8 kf;
         ring_read_k8<kWaitK>(kf, sbase(0) + k8_lane_off(lane), sbase(0) + 8192 + 32 * (lane >> 4));
         issue_k(min(DEPTH, nb - 1), 0);
-        step_scores8<RB>(kf, qf, ws, pr, lane, step_t0(0), L, kv, growbase, R, G, a.scale_log2);
+        step_scores8<RB>(kf, qf, ws, pr, lane, step_t0(0), mk, a.scale_log2);
         sv[0] = kf.sv[0];
         sv[1] = kf.sv[1];
       }
@@ -887,7 +907,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         step_pv8<RB, false>(vf, sv, pr, ws, lane, t0, kv);
         sv[0] = kf.sv[0];
         sv[1] = kf.sv[1];
-        const bool any = mask_check<RB>(x, lmx, ws, rowlim, lane, step_t0(kk + 1));
+        const bool any = mask_check<RB>(x, lmx, ws, mk, lane, step_t0(kk + 1));
         softmax_pf<RB>(x, ws, lsum, pr);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
@@ -911,7 +931,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const int pid = bstart == 0 ? pid_first : page_ids(bstart);
       const int nb = min(kWave, my_steps - bstart);
-      auto step_t0 = [&](int kk) { return chunk_lo + kStep * (ts + (bstart + kk) * NTS); };
+      auto step_t0 = [&](int kk) { return live_t0(ts + (bstart + kk) * NTS); };
       auto step_base = [&](int kk, const _Float16* pool) { return pool + tok_row(pid, bstart, kk) * kHeadDim; };
       // DEPTH steps in flight per wave in its ring, one in registers. Order
       // of DMA issue: K(k+DEPTH) right after K(k) is read, V(k+DEPTH) right
@@ -938,7 +958,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         KFrag kf;
         ring_read8<kWait, false, 64>(kf.k, ring_lds + stage(0) + k_lane_off(lane));
         dma_k<0, 8>(step_base(min(DEPTH, nb - 1), kpool), ring + stage(0), lane);
-        step_scores<RB>(kf, qf, ws, pb, lane, step_t0(0), L, kv, growbase, R, G, a.scale_log2);
+        step_scores<RB>(kf, qf, ws, pb, lane, step_t0(0), mk, a.scale_log2);
       }
       for (int kk = 0; kk + 1 < nb; ++kk) {
         const int t0 = step_t0(kk);
@@ -953,7 +973,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         scores_mfma<RB>(kf, qf, lane, a.scale_log2, x);
         // (a step before the wave's last of the batch ends below kv_len)
         step_pv<RB, false>(vf, pb, ws, lane, t0, kv);
-        const bool any = mask_check<RB>(x, lmx, ws, rowlim, lane, step_t0(kk + 1));
+        const bool any = mask_check<RB>(x, lmx, ws, mk, lane, step_t0(kk + 1));
         softmax_p<RB>(x, ws, lsum, pb);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;

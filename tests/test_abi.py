@@ -198,3 +198,13 @@ def test_topk_rejects_bad_arguments_without_launch():
     assert lib.sv_topk_candidates(fake, 8, 1 << 20, 16, fake, fake, fake, 1 << 30, None) == B.SV_ERR_UNSUPPORTED
     assert lib.sv_topk_candidates(fake, 8, 248320, 16, fake, fake, fake, need - 1, None) == B.SV_ERR_WORKSPACE_TOO_SMALL
     assert lib.sv_topk_candidates(None, 8, 248320, 16, fake, fake, fake, need, None) == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_window_parameters_are_validated():
+    with pytest.raises(B.SvError) as e:
+        B.sv_verify_plan(_p(window=-1))
+    assert e.value.status == B.SV_ERR_INVALID_ARGUMENT
+    with pytest.raises(B.SvError) as e:
+        B.sv_verify_plan(_p(sink=4))  # a sink without a window
+    assert e.value.status == B.SV_ERR_INVALID_ARGUMENT
+    assert B.sv_verify_plan(_p(window=2048, sink=4))[0] >= 1
