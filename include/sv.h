@@ -318,7 +318,7 @@ size_t sv_rejection_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t
  *   accept_len, token_ids [batch] int32 (written)
  *   kv_lens_in, kv_lens_out  both NULL, or both [batch] int32 (may alias)
  *   workspace    sv_rejection_accept_workspace_bytes() bytes, 256-byte aligned
- * Arithmetic is fp32; q_len <= 64; batch * q_len <= 65535. The three NULL
+ * Arithmetic is fp32; q_len <= 64; batch * q_len <= 65535; vocab <= 524,288. The three NULL
  * draft pointers are allowed when q_len == 1.
  */
 sv_status sv_rejection_accept(const float* logits, const int32_t* draft_ids, const float* draft_probs,

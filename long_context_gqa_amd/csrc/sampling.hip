@@ -47,16 +47,28 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
-// Statistics (M, 1/S) of row r from its slices' (m, s).
-__device__ __forceinline__ void row_stat(const float2* __restrict__ ws1, int n_slices, size_t row, float* M,
-                                         float* invS) {
+// Statistics (M, 1/S) of row `row` from its slices' (m, s), by one wave: lane
+// k takes slice k (n_slices <= 64), then the wave combines; every lane gets
+// the result.
+__device__ __forceinline__ void row_stat_wave(const float2* __restrict__ ws1, int n_slices, size_t row, int lane,
+                                              float* M, float* invS) {
   Stat t{-INFINITY, 0.f};
-  for (int k = 0; k < n_slices; ++k) {
-    const float2 v = ws1[row * n_slices + k];
-    t = combine(t, Stat{v.x, v.y});
+  if (lane < n_slices) {
+    const float2 v = ws1[row * n_slices + lane];
+    t = Stat{v.x, v.y};
   }
+  t = wave_stat(t);
   *M = t.m;
   *invS = t.s > 0.f ? 1.f / t.s : 0.f;
+}
+
+__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
 }
 
 }  // namespace
@@ -108,15 +120,34 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(const float* __rest
   }
 }
 
-// Whether draft j of request b passes its test u_j * q_j(d) < p_j(d) (an id
-// outside the vocabulary never does).
-__device__ __forceinline__ bool keeps(const SampleLaunch& a, int b, int j, float M, float invS) {
-  const size_t row = (size_t)b * a.q_len + j;
-  const int d = a.draft_ids[(size_t)b * (a.q_len - 1) + j];
-  if (d < 0 || d >= a.vocab) return false;
-  const float p = __builtin_amdgcn_exp2f(a.logits[row * a.vocab + d] * a.c - M) * invS;
-  const float qd = a.draft_probs[((size_t)b * (a.q_len - 1) + j) * a.vocab + d];
-  return a.u_accept[(size_t)b * (a.q_len - 1) + j] * qd < p;
+// Request b's row statistics (in LDS) and whether each draft passes its test
+// u_j * q_j(d) < p_j(d) (an id outside the vocabulary never does): the
+// tested elements are loaded for all drafts at once, then each wave combines
+// the slice statistics of every fourth row.
+__device__ __forceinline__ void request_tests(const SampleLaunch& a, int b, float* M, float* invS, int* keep) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  __shared__ float s_ld[kMaxSampleRows], s_qu[kMaxSampleRows];
+  for (int j = tid; j < a.q_len - 1; j += kThreads) {
+    const int d = a.draft_ids[(size_t)b * (a.q_len - 1) + j];
+    const bool ok = d >= 0 && d < a.vocab;
+    s_ld[j] = ok ? a.logits[((size_t)b * a.q_len + j) * a.vocab + d] : 0.f;
+    // u * q(d), or +inf for an id that is never kept
+    s_qu[j] = ok ? a.u_accept[(size_t)b * (a.q_len - 1) + j] *
+                       a.draft_probs[((size_t)b * (a.q_len - 1) + j) * a.vocab + d]
+                 : INFINITY;
+  }
+  for (int j = wave; j < a.q_len; j += kWavesPerGroup) {
+    float m, is;
+    row_stat_wave(a.ws1, a.n_slices, (size_t)b * a.q_len + j, lane, &m, &is);
+    if (lane == 0) {
+      M[j] = m;
+      invS[j] = is;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < a.q_len; j += kThreads)
+    keep[j] = (j < a.q_len - 1) ? (int)(s_qu[j] < __builtin_amdgcn_exp2f(s_ld[j] * a.c - M[j]) * invS[j]) : 0;
+  __syncthreads();
 }
 
 template <bool VEC4>
@@ -127,14 +158,7 @@ __global__ __launch_bounds__(kThreads) void walk_residual_kernel(SampleLaunch a)
   __shared__ int s_acc;
   // every row's statistics and every draft's test in parallel; the walk
   // then stops at the first draft that fails (the same in every workgroup)
-  for (int j = tid; j < a.q_len; j += kThreads) {
-    float m, is;
-    row_stat(a.ws1, a.n_slices, (size_t)b * a.q_len + j, &m, &is);
-    M[j] = m;
-    invS[j] = is;
-    keep[j] = (j < a.q_len - 1) ? (int)keeps(a, b, j, m, is) : 0;
-  }
-  __syncthreads();
+  request_tests(a, b, M, invS, keep);
   if (tid == 0) {
     int acc = 0;
     while (acc < a.q_len - 1 && keep[acc]) ++acc;
@@ -195,45 +219,47 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(SampleLaunch a) {
   const int A = a.ws_acc[b];
   const bool residual = A < a.q_len - 1;
   const size_t row = (size_t)b * a.q_len + A;
-  if (tid == 0) {
-    row_stat(a.ws1, a.n_slices, row, &s_M, &s_iS);
-    // totals of the residual's slices; a residual that is zero everywhere
-    // (p = q on that row) falls back to p
-    float tot = 0.f;
-    for (int k = 0; k < a.n_slices; ++k) tot += a.ws2[(size_t)b * a.n_slices + k];
+  if (tid < kWave) {
+    // wave 0: the row's statistics, the slices' weights (the residual's, or
+    // p's from the statistics when the residual is zero everywhere or every
+    // draft was kept), the total, and the slice where the cumulative weight
+    // passes u_final * total (a prefix scan over the slices, one per lane)
+    const int lane = tid;
+    float M, iS;
+    row_stat_wave(a.ws1, a.n_slices, row, lane, &M, &iS);
+    const bool in = lane < a.n_slices;
+    const float wr = in ? a.ws2[(size_t)b * a.n_slices + lane] : 0.f;
+    float tot = wave_sum_f(wr);
     int mode = residual ? 1 : 0;
     if (residual && !(tot > 0.f)) mode = 0;
+    float w = wr;
     if (mode == 0 && residual) {
       // p's slice sums from the row statistics
-      tot = 0.f;
-      for (int k = 0; k < a.n_slices; ++k) {
-        const float2 v = a.ws1[row * a.n_slices + k];
-        tot += v.y * __builtin_amdgcn_exp2f(v.x - s_M) * s_iS;
+      w = 0.f;
+      if (in) {
+        const float2 v = a.ws1[row * a.n_slices + lane];
+        w = v.y * __builtin_amdgcn_exp2f(v.x - M) * iS;
       }
+      tot = wave_sum_f(w);
     }
     const float target = a.u_final[b] * tot;
-    float cum = 0.f;
-    int k = -1, last = 0;
-    for (int j = 0; j < a.n_slices; ++j) {
-      float sj;
-      if (mode == 1 || !residual) sj = a.ws2[(size_t)b * a.n_slices + j];
-      else {
-        const float2 v = a.ws1[row * a.n_slices + j];
-        sj = v.y * __builtin_amdgcn_exp2f(v.x - s_M) * s_iS;
-      }
-      if (sj > 0.f) last = j;
-      if (k < 0 && cum + sj > target) {
-        k = j;
-        break;
-      }
-      cum += sj;
+    const float cum = wave_incl_scan(w, lane);
+    const uint64_t past = __ballot(in && cum > target);
+    const uint64_t pos = __ballot(in && w > 0.f);
+    // the first slice past the target (uniform across the wave), or when
+    // rounding put the target past the total, the last positive weight
+    const int k = past ? __builtin_ctzll(past) : (pos ? 63 - __builtin_clzll(pos) : 0);
+    const float base = __shfl(cum, k) - __shfl(w, k);
+    if (lane == 0) {
+      s_last = past ? 0 : 1;
+      s_k = k;
+      s_base = past ? base : 0.f;
+      s_target = target;
+      s_mode = mode;
+      s_best = INT32_MAX;
+      s_M = M;
+      s_iS = iS;
     }
-    s_last = (k < 0) ? 1 : 0;  // rounding put the target past the total: take the last positive weight
-    s_k = (k < 0) ? last : k;
-    s_base = cum;
-    s_target = target;
-    s_mode = mode;
-    s_best = INT32_MAX;
   }
   __syncthreads();
   const float* lp = a.logits + row * a.vocab;

@@ -501,6 +501,8 @@ sv_status sv_rejection_accept(const float* logits, const int32_t* draft_ids, con
   if (batch < 1 || q_len < 1 || vocab < 1)
     return fail(SV_ERR_INVALID_ARGUMENT, "batch, q_len and vocab must be >= 1");
   if (q_len > sv::kMaxSampleRows) return fail(SV_ERR_UNSUPPORTED, "q_len must be <= %d", sv::kMaxSampleRows);
+  if ((long long)vocab > 64LL * sv::kSampleSlice)
+    return fail(SV_ERR_UNSUPPORTED, "vocab must be <= %d", 64 * sv::kSampleSlice);
   if ((long long)batch * q_len > 65535) return fail(SV_ERR_UNSUPPORTED, "batch * q_len must be <= 65535");
   if (!(temperature > 0.f) || temperature > 1e30f)
     return fail(SV_ERR_INVALID_ARGUMENT, "temperature must be positive and finite");
