@@ -341,7 +341,7 @@ size_t sv_topk_candidates_workspace_bytes(int32_t rows, int32_t vocab, int32_t k
  *     out_values[row][j]   = logits[row][out_ids[row][j]]
  *
  *   logits      [rows, vocab] fp32 (NaN order is unspecified; -inf allowed)
- *   k           1..16, k <= vocab; vocab <= 512/k * 8192 columns (262,144 at k = 16)
+ *   k           1..16, k <= vocab; vocab <= 512/k * 8,192 columns (262,144 at k = 16)
  *   out_ids     [rows, k] int32 (written); out_values [rows, k] fp32 (written)
  *   workspace   sv_topk_candidates_workspace_bytes() bytes
  * rows <= 65535. The same kernels give the top k of any slice union, so a

@@ -574,7 +574,10 @@ sv_status sv_topk_candidates(const float* logits, int32_t rows, int32_t vocab, i
   a.rows = rows;
   a.vocab = vocab;
   a.k = k;
-  a.n_slices = (int)slices;
+  // few rows: wider slices (fewer, fuller workgroups); the workspace is sized
+  // for the narrow ones
+  a.slice = rows <= 64 ? sv::kTopkSliceWide : sv::kTopkSlice;
+  a.n_slices = (int)(((long long)vocab + a.slice - 1) / a.slice);
   a.ws = static_cast<float2*>(workspace);
   a.out_ids = out_ids;
   a.out_vals = out_values;

@@ -1,8 +1,9 @@
 // Top-k candidate selection over the vocabulary: each row's k highest
 // logits, value descending, the lower index first among equal values.
 //
-// Stage 1 (topk_slice): one workgroup per (row, slice of 8,192 columns). Each
-//   lane holds 32 of the slice's values in registers; each wave finds its
+// Stage 1 (topk_slice): one workgroup per (row, slice of 8,192 columns, or
+//   16,384 when there are few rows to spread). Each lane holds 32 (64) of the
+//   slice's values in registers; each wave finds its
 //   best k through a threshold (the k-th best lane maximum), compacts the few
 //   values that can still be in the answer, and sorts them with a 64-lane
 //   bitonic network; wave 0 sorts the 4k wave winners the same way. The
@@ -37,23 +38,65 @@ __device__ __forceinline__ Cand wave_best(Cand x) {
   return x;
 }
 
-constexpr int kPerLane = kTopkSlice / kThreads;  // 32 values per lane
 constexpr Cand kNone = {-INFINITY, INT32_MAX};
+
+// The value of lane (lane ^ J) without the LDS crossbar: DPP quad
+// permutations (xor 1, 2), row shifts (xor 4: lane +4 where bit 2 is clear,
+// -4 where set), a row rotation (xor 8), and the gfx950 row/half swaps
+// (xor 16, 32: the swapped copy of the other row or half).
+template <int J>
+__device__ __forceinline__ int xor_lane(int x, int lane) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const int up = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0xF, false);  // row_shl:4 (lane + 4)
+    const int dn = __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false);  // row_shr:4 (lane - 4)
+    return (lane & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (J == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? (int)p[0] : (int)p[1];
+  } else {
+    static_assert(J == 32, "xor distance");
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? (int)p[0] : (int)p[1];
+  }
+}
+
+template <int J>
+__device__ __forceinline__ Cand xor_cand(Cand c, int lane) {
+  return Cand{__int_as_float(xor_lane<J>(__float_as_int(c.v), lane)), xor_lane<J>(c.i, lane)};
+}
+
+// One compare-exchange stage of the bitonic network: run length K, distance J.
+template <int K, int J>
+__device__ __forceinline__ Cand bitonic_stage(Cand c, int lane) {
+  const Cand o = xor_cand<J>(c, lane);
+  const bool best_first = (lane & K) == 0 || K == kWave;  // this run sorts best first
+  const bool low = (lane & J) == 0;                         // lower lane of the pair
+  const bool take = (low == best_first) ? beats(o, c) : beats(c, o);
+  return take ? o : c;
+}
+
+template <int K, int J>
+__device__ __forceinline__ Cand bitonic_merge(Cand c, int lane) {
+  c = bitonic_stage<K, J>(c, lane);
+  if constexpr (J > 1) c = bitonic_merge<K, J / 2>(c, lane);
+  return c;
+}
 
 // Sort one candidate per lane across the wave, best first (bitonic network
 // over lane ids; indices are unique, so every pair has one better member).
 __device__ __forceinline__ Cand bitonic64(Cand c, int lane) {
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const Cand o{__shfl_xor(c.v, j), __shfl_xor(c.i, j)};
-      const bool best_first = (lane & k) == 0 || k == kWave;  // this run sorts best first
-      const bool low = (lane & j) == 0;                         // lower lane of the pair
-      const bool take = (low == best_first) ? beats(o, c) : beats(c, o);
-      if (take) c = o;
-    }
-  }
+  c = bitonic_merge<2, 1>(c, lane);
+  c = bitonic_merge<4, 2>(c, lane);
+  c = bitonic_merge<8, 4>(c, lane);
+  c = bitonic_merge<16, 8>(c, lane);
+  c = bitonic_merge<32, 16>(c, lane);
+  c = bitonic_merge<64, 32>(c, lane);
   return c;
 }
 
@@ -73,7 +116,8 @@ __device__ __forceinline__ void wave_topk(const float (&v)[N], const int (&idx)[
     if (beats(c, lb)) lb = c;
   }
   const Cand srt = bitonic64(lb, lane);
-  const Cand t{__shfl(srt.v, k - 1), __shfl(srt.i, k - 1)};
+  const Cand t{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(srt.v), k - 1)),
+               __builtin_amdgcn_readlane(srt.i, k - 1)};
   int count = 0;
 #pragma unroll
   for (int u = 0; u < N; ++u) {
@@ -119,25 +163,78 @@ __device__ __forceinline__ void wave_topk(const float (&v)[N], const int (&idx)[
 
 }  // namespace
 
-template <bool VEC4>
+// Column of this lane's value u in a slice starting at lo (increasing in u).
+__device__ __forceinline__ int slice_col(int lo, int tid, int u) { return lo + 4 * (tid + (u / 4) * kThreads) + u % 4; }
+
+// The slice stage of one wave: its best k of the lane values v (column
+// slice_col(lo, tid, u), valid below hi), written to out[0..k-1]. As
+// wave_topk, specialised: a lane's columns increase with u, so its maximum
+// needs value compares only (the first of equal values has the lowest
+// column), and the values that can still be in the answer are found by a
+// cheap test against the threshold's value first (v >= t.v), the exact rank
+// test only when some lane passes it.
+template <int NPL>
+__device__ __forceinline__ void slice_wave_topk(const float (&v)[NPL], int lo, int hi, int tid, int k, Cand* out,
+                                                Cand* buf, int lane) {
+  Cand lb = kNone;
+  if (slice_col(lo, tid, 0) < hi) {
+    lb = Cand{v[0], slice_col(lo, tid, 0)};
+#pragma unroll
+    for (int u = 1; u < NPL; ++u)
+      if (v[u] > lb.v) lb = Cand{v[u], slice_col(lo, tid, u)};  // (past hi, v is -inf and never wins)
+  }
+  const Cand srt = bitonic64(lb, lane);
+  const Cand t{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(srt.v), k - 1)),
+               __builtin_amdgcn_readlane(srt.i, k - 1)};
+  int count = 0;
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) {
+    if (__ballot(v[u] >= t.v)) {  // (uniform) some lane may hold a candidate here
+      const Cand c{v[u], slice_col(lo, tid, u)};
+      const bool pred = c.i < hi && !beats(t, c);
+      const uint64_t m = __ballot(pred);
+      if (pred) buf[count + __popcll(m & ((1ull << lane) - 1ull))] = c;
+      count += __popcll(m);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (count <= kWave) {
+    Cand c = lane < count ? buf[lane] : kNone;
+    c = bitonic64(c, lane);
+    if (lane < k) out[lane] = c;
+  } else {
+    // rare (many values tied or clustered in a few lanes): k rounds of a
+    // wave maximum over the compacted values
+    Cand mine = kNone;
+    for (int e = lane; e < count; e += kWave)
+      if (beats(buf[e], mine)) mine = buf[e];
+    for (int r = 0; r < k; ++r) {
+      const Cand w = wave_best(mine);
+      if (lane == 0) out[r] = w;
+      if (w.i != INT32_MAX && mine.i == w.i) {
+        mine = kNone;
+        for (int e = lane; e < count; e += kWave)
+          if (buf[e].i != w.i && beats(buf[e], mine) && beats(w, buf[e])) mine = buf[e];
+      }
+    }
+  }
+}
+
+// NPL values per lane: slices of NPL * 256 columns.
+template <bool VEC4, int NPL>
 __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __restrict__ logits, int vocab, int k,
                                                               int n_slices, float2* ws) {
   const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
-  const int lo = sl * kTopkSlice, hi = min(lo + kTopkSlice, vocab);
+  const int lo = sl * NPL * kThreads, hi = min(lo + NPL * kThreads, vocab);
   const float* rp = logits + (size_t)row * vocab;
-  // value u of this lane is column lo + 4*(tid + 256*(u/4)) + u%4
-  float v[kPerLane];
-  int idx[kPerLane];
-#pragma unroll
-  for (int u = 0; u < kPerLane; ++u) {
-    const int col = lo + 4 * (tid + (u / 4) * kThreads) + u % 4;
-    idx[u] = col < hi ? col : INT32_MAX;
-  }
+  float v[NPL];
   if (VEC4) {
 #pragma unroll
-    for (int g = 0; g < kPerLane / 4; ++g) {
-      const int col = lo + 4 * (tid + g * kThreads);
+    for (int g = 0; g < NPL / 4; ++g) {
+      const int col = slice_col(lo, tid, 4 * g);
       const float4 x = col < hi ? *reinterpret_cast<const float4*>(rp + col)
                                 : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       v[4 * g] = x.x;
@@ -147,11 +244,14 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __res
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < kPerLane; ++u) v[u] = idx[u] != INT32_MAX ? rp[idx[u]] : -INFINITY;
+    for (int u = 0; u < NPL; ++u) {
+      const int col = slice_col(lo, tid, u);
+      v[u] = col < hi ? rp[col] : -INFINITY;
+    }
   }
-  __shared__ Cand buf[kWavesPerGroup][kMaxTopk * kPerLane];
+  __shared__ Cand buf[kWavesPerGroup][kMaxTopk * NPL];
   __shared__ Cand wl[kWavesPerGroup * kMaxTopk];
-  wave_topk<kPerLane>(v, idx, k, &wl[wave * k], buf[wave], lane);
+  slice_wave_topk<NPL>(v, lo, hi, tid, k, &wl[wave * k], buf[wave], lane);
   __syncthreads();
   if (wave == 0) {
     // the best k of the 4k wave winners (k <= 16: one per lane)
@@ -196,11 +296,19 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const float2* __re
 
 void launch_topk(const TopkLaunch& a, hipStream_t s) {
   dim3 g1(a.n_slices, a.rows);
-  if (a.vocab % 4 == 0)
-    hipLaunchKernelGGL((topk_slice_kernel<true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.k, a.n_slices, a.ws);
+  const bool vec4 = a.vocab % 4 == 0, wide = a.slice == kTopkSliceWide;
+  if (vec4 && wide)
+    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSliceWide / kThreads>), g1, dim3(kThreads), 0, s, a.logits,
+                       a.vocab, a.k, a.n_slices, a.ws);
+  else if (vec4)
+    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSlice / kThreads>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
+                       a.k, a.n_slices, a.ws);
+  else if (wide)
+    hipLaunchKernelGGL((topk_slice_kernel<false, kTopkSliceWide / kThreads>), g1, dim3(kThreads), 0, s, a.logits,
+                       a.vocab, a.k, a.n_slices, a.ws);
   else
-    hipLaunchKernelGGL((topk_slice_kernel<false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.k, a.n_slices,
-                       a.ws);
+    hipLaunchKernelGGL((topk_slice_kernel<false, kTopkSlice / kThreads>), g1, dim3(kThreads), 0, s, a.logits,
+                       a.vocab, a.k, a.n_slices, a.ws);
   hipLaunchKernelGGL(topk_merge_kernel, dim3((a.rows + kWavesPerGroup - 1) / kWavesPerGroup), dim3(kThreads), 0, s,
                      a.ws, a.rows, a.n_slices, a.k, a.out_ids, a.out_vals);
 }

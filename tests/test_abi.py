@@ -191,7 +191,7 @@ def test_topk_rejects_bad_arguments_without_launch():
     lib = B.lib()
     fake = 1 << 40
     need = lib.sv_topk_candidates_workspace_bytes(8, 248320, 16)
-    assert need == 8 * 31 * 16 * 8
+    assert need == 8 * 31 * 16 * 8  # a list of 16 (value, index) pairs per (row, 8,192-column slice)
     assert lib.sv_topk_candidates(fake, 8, 248320, 17, fake, fake, fake, need, None) == B.SV_ERR_UNSUPPORTED
     assert lib.sv_topk_candidates(fake, 8, 248320, 0, fake, fake, fake, need, None) == B.SV_ERR_UNSUPPORTED
     assert lib.sv_topk_candidates(fake, 8, 10, 11, fake, fake, fake, need, None) == B.SV_ERR_INVALID_ARGUMENT

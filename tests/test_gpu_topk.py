@@ -37,16 +37,19 @@ def check(x, k, what=""):
 @pytest.mark.parametrize("rows,vocab,k", [
     (8, 248_320, 16), (64, 248_320, 16), (8, 248_320, 1), (8, 248_320, 5),
     (5, 1003, 16), (3, 100, 16), (4, 8192 * 3 + 5, 16), (2, 10, 10), (7, 8192, 16),
+    # more than 64 rows: the narrower slices
+    (100, 248_320, 16), (80, 8192 * 2 + 3, 7), (65, 1003, 16),
 ])
 def test_random_rows(rows, vocab, k):
     rng = np.random.default_rng(rows * 1000 + vocab % 1000 + k)
     check((rng.standard_normal((rows, vocab)) * 3).astype(np.float32), k, "random")
 
 
+@pytest.mark.parametrize("rows", [6, 70])
 @pytest.mark.parametrize("vocab", [248_320, 1003])
-def test_ties_everywhere_lowest_index_first(vocab):
-    rng = np.random.default_rng(vocab)
-    x = rng.integers(-3, 4, (6, vocab)).astype(np.float32)
+def test_ties_everywhere_lowest_index_first(vocab, rows):
+    rng = np.random.default_rng(vocab + rows)
+    x = rng.integers(-3, 4, (rows, vocab)).astype(np.float32)
     check(x, 16, "integer ties")
     z = np.zeros((2, vocab), dtype=np.float32)
     ids, _ = run(z, 16)
