@@ -317,14 +317,14 @@ class RaggedVerifyCall:
     ``max_q_len`` is the largest width."""
 
     def __init__(self, q, q_start, k_pages, v_pages, page_table, kv_lens, max_q_len, max_kv_len,
-                 k_scales=None, v_scales=None, sm_scale=None, num_splits=0, with_lse=True):
+                 k_scales=None, v_scales=None, sm_scale=None, num_splits=0, with_lse=True, window=0, sink=0):
         dev = q.device
         B = kv_lens.shape[0]
         Hq, D = q.shape[1], q.shape[2]
         Hkv, P = k_pages.shape[1], k_pages.shape[2]
         dtype = SV_KV_FP8_E4M3 if k_pages.dtype == torch.uint8 else SV_KV_FP16
         self.params = make_params(B, max_q_len, Hq, Hkv, D, P, k_pages.shape[0], page_table.shape[1],
-                                  max_kv_len, dtype, sm_scale, num_splits)
+                                  max_kv_len, dtype, sm_scale, num_splits, window, sink)
         self.q_start = q_start
         self.inputs = (q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens)
         self.out = torch.empty_like(q)

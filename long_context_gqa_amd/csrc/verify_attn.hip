@@ -95,9 +95,9 @@ struct WaveState {
 };
 
 // The keys each of a lane's rows sees: t < lim (causal and tail limit) and,
-// with a sliding window, t >= lo or t < sink (the leading sink positions).
-// Without a window lo is INT_MIN.
-template <int RB>
+// with a sliding window (WIN), t >= lo or t < sink (the leading sink
+// positions). Full attention compiles without the window terms.
+template <int RB, bool WIN>
 struct RowMask {
   int lim[RB];
   int lo[RB];
@@ -106,23 +106,26 @@ struct RowMask {
 
 // Masking of one step's scores (lane holds tokens t0 + 4*(lane/16) + i of row
 // lane%16 in each row block), without branches.
-template <int RB>
-__device__ __forceinline__ void apply_mask(float (&x)[RB][4], const RowMask<RB>& mk, int lane, int t0) {
+template <int RB, bool WIN>
+__device__ __forceinline__ void apply_mask(float (&x)[RB][4], const RowMask<RB, WIN>& mk, int lane, int t0) {
   const int tok = t0 + 4 * (lane >> 4);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tok + i;
-      x[rb][i] = (t >= mk.lim[rb] || (t < mk.lo[rb] && t >= mk.sink)) ? -INFINITY : x[rb][i];
+      if constexpr (WIN)
+        x[rb][i] = (t >= mk.lim[rb] || (t < mk.lo[rb] && t >= mk.sink)) ? -INFINITY : x[rb][i];
+      else
+        x[rb][i] = t >= mk.lim[rb] ? -INFINITY : x[rb][i];
     }
 }
 
 // Online-softmax update of one step from the scaled scores x (log2 units):
 // masking, the lazy reference, the running sum, and p.
-template <int RB>
+template <int RB, bool WIN>
 __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& ws, float (&p)[RB][4],
-                                             int lane, int t0, const RowMask<RB>& mk) {
+                                             int lane, int t0, const RowMask<RB, WIN>& mk) {
   apply_mask<RB>(x, mk, lane, t0);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -151,10 +154,10 @@ __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& w
 }
 
 // Scores of one fp16 step and the fp16 P^T fragments.
-template <int RB>
+template <int RB, bool WIN>
 __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __restrict__ qf,
                                             WaveState<RB>& ws, half4_t (&pb)[RB], int lane, int t0,
-                                            const RowMask<RB>& mk, float scale_log2) {
+                                            const RowMask<RB, WIN>& mk, float scale_log2) {
   float x[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -193,9 +196,9 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
 //                 matrix ops; redone after a move);
 //   rescale_o     (rare) O *= alpha, after step k's PV was accumulated at the
 //                 old reference.
-template <int RB>
+template <int RB, bool WIN>
 __device__ __forceinline__ bool mask_check(float (&x)[RB][4], float (&lmx)[RB], const WaveState<RB>& ws,
-                                           const RowMask<RB>& mk, int lane, int t0) {
+                                           const RowMask<RB, WIN>& mk, int lane, int t0) {
   apply_mask<RB>(x, mk, lane, t0);
   bool bump = false;
 #pragma unroll
@@ -294,10 +297,10 @@ __device__ __forceinline__ float half_at(const u32x4 (&h)[2], int idx) {
 
 // Scores of one FP8 step: per 64-channel block, two MFMAs on the converted
 // K, then S = sum_b scale_b * partial_b.
-template <int RB>
+template <int RB, bool WIN>
 __device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __restrict__ qf,
                                              WaveState<RB>& ws, float (&p)[RB][4], int lane, int t0,
-                                             const RowMask<RB>& mk, float scale_log2) {
+                                             const RowMask<RB, WIN>& mk, float scale_log2) {
   u32x4 kc[8];
 #pragma unroll
   for (int bk = 0; bk < 4; ++bk) {
@@ -690,7 +693,7 @@ struct Smem {
   static constexpr int BIG = RBYTES > OBYTES ? RBYTES : OBYTES;
 };
 
-template <int RB, bool FP8, int DEPTH>
+template <int RB, bool FP8, int DEPTH, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   static_assert(DEPTH == 1 || DEPTH == 2, "one or two steps in flight");
   using SM = Smem<RB, FP8, DEPTH>;
@@ -747,8 +750,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // Key chunks tile the block's live 16-token steps (all steps from position
   // 0, or with a sliding window the sink steps then the window steps):
   // chunk `split` holds steps [split*cs, split*cs + n_steps).
-  int n_sink, w0;
-  const int total = live_steps(kv, L, W, S, &n_sink, &w0);
+  int n_sink = 0, w0 = 0;
+  const int total = WIN ? live_steps(kv, L, W, S, &n_sink, &w0) : (kv > 0 ? (kv + kStep - 1) / kStep : 0);
   const int cs = a.chunk / kStep;
   const int n_chunks = total > 0 ? (total + cs - 1) / cs : 1;
   if (split >= n_chunks) return;  // whole group: nothing of this request here
@@ -757,6 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const int n_steps = min(total - k_base, cs) > 0 ? min(total - k_base, cs) : 0;
   auto live_t0 = [&](int j) {
     const int k = k_base + j;
+    if constexpr (!WIN) return kStep * k;
     return k < n_sink ? kStep * k : w0 + kStep * (k - n_sink);
   };
   if (tid == 0) s_flag = 0;
@@ -844,13 +848,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // the keys each of this lane's rows sees: row r (block row i = r/G, at
   // position L + i) sees t <= L + i and, with a window, t > L + i - W or t < S;
   // padding rows see every key
-  RowMask<RB> mk;
+  RowMask<RB, WIN> mk;
   mk.sink = S;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = growbase + rb * 16 + (lane & 15);
     mk.lim[rb] = r < R ? min(L + r / G + 1, kv) : kv;
-    mk.lo[rb] = (W > 0 && r < R) ? L + r / G + 1 - W : INT32_MIN;
+    mk.lo[rb] = r < R ? L + r / G + 1 - W : INT32_MIN;
   }
   if constexpr (FP8) {
     // ---- FP8: each wave owns its token steps and a private one-step ring ----
@@ -1113,29 +1117,30 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   if (tid == 0 && s_flag && a.flags) atomicOr(a.flags, s_flag);
 }
 
+template <bool FP8, int DEPTH, bool WIN>
+void launch_rb(const AttnArgs& a, int rb, dim3 grid, hipStream_t s) {
+  const dim3 block(kThreads);
+  if (rb == 1 && DEPTH == 1) hipLaunchKernelGGL((verify_attn_kernel<1, FP8, 1, WIN>), grid, block, 0, s, a);
+  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, FP8, DEPTH, WIN>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((verify_attn_kernel<3, FP8, DEPTH, WIN>), grid, block, 0, s, a);
+}
+
+template <bool FP8, bool WIN>
+void launch_depth(const AttnArgs& a, int rb, hipStream_t s) {
+  // one workgroup per unit; with two row blocks, 16 ids per 8 units, and the
+  // two workgroups on the same keys (rb is then 2 or 3) keep two steps in flight
+  if (a.row_blocks == 2) launch_rb<FP8, 2, WIN>(a, rb, dim3(2 * ((a.units + 7) / 8 * 8)), s);
+  else launch_rb<FP8, 1, WIN>(a, rb, dim3(a.units), s);
+}
+
 void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s) {
-  // one workgroup per unit; with two row blocks, 16 ids per 8 units
-  const int n = a.row_blocks == 2 ? 2 * ((a.units + 7) / 8 * 8) : a.units;
-  dim3 grid(n), block(kThreads);
-  // two workgroups on the same keys (rb is then 2 or 3): two steps in flight
-  if (a.row_blocks == 2) {
-    if (fp8) {
-      if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, true, 2>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((verify_attn_kernel<3, true, 2>), grid, block, 0, s, a);
-    } else {
-      if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false, 2>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((verify_attn_kernel<3, false, 2>), grid, block, 0, s, a);
-    }
-    return;
-  }
+  const bool win = a.window > 0;
   if (fp8) {
-    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, true, 1>), grid, block, 0, s, a);
-    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, true, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((verify_attn_kernel<3, true, 1>), grid, block, 0, s, a);
+    if (win) launch_depth<true, true>(a, rb, s);
+    else launch_depth<true, false>(a, rb, s);
   } else {
-    if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false, 1>), grid, block, 0, s, a);
-    else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((verify_attn_kernel<3, false, 1>), grid, block, 0, s, a);
+    if (win) launch_depth<false, true>(a, rb, s);
+    else launch_depth<false, false>(a, rb, s);
   }
 }
 

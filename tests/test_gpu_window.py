@@ -76,8 +76,7 @@ def test_window_with_widths_per_request():
     q = W.pack_rows(x.q, 8, widths)
     qs = W.row_offsets(widths)
     c = B.RaggedVerifyCall(q, qs.cuda(), x.k_pages, x.v_pages, x.page_table.cuda(), kv.cuda(), 8,
-                           int(x.kv_lens.max()), sm_scale=x.sm_scale, num_splits=3)
-    c.params.window, c.params.sink = Wn, S
+                           int(x.kv_lens.max()), sm_scale=x.sm_scale, num_splits=3, window=Wn, sink=S)
     out, lse = c.run()
     torch.cuda.synchronize()
     h = host(x)
