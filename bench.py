@@ -6,7 +6,7 @@ greedy acceptance over the block's fp32 logits (sv_greedy_accept), on seeded
 synthetic inputs already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--variant literal] [--ragged] [--stochastic] [--topk]
-                    [--window W --sink S]
+                    [--window W --sink S] [--extend 64,256]
 
 Prints one JSON line. `value` is the effective HBM bandwidth of the whole step
 (algorithmic bytes of attention + accept / step time). The `roofline` object
@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify-attn effective HBM GB/s (% of peak) at q=8, 512K ctx; verified tok/s"
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_FP16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 
 
 def log(*a):
@@ -65,6 +66,9 @@ def parse():
     ap.add_argument("--window", type=int, default=0,
                     help="also time the sink + sliding-window verify with this window (positions)")
     ap.add_argument("--sink", type=int, default=0, help="leading sink positions for --window")
+    ap.add_argument("--extend", default=None,
+                    help="also time extend chunks of these widths (comma list, up to 512 rows per request) "
+                         "over the workload's cache, against the fp16 MFMA peak")
     ap.add_argument("--traffic", default=None,
                     help="JSON with measured HBM bytes per verify_attn launch (default: the one under "
                          "profiles/ for this workload, used only while the kernel source is unchanged)")
@@ -289,6 +293,34 @@ def main():
         log(f"[bench] window {args.window} sink {args.sink}: {us:.2f} us over {sum(vis)} visible keys")
         del wc
 
+    ext = None
+    if args.extend:
+        ext = []
+        for qe in [int(v) for v in args.extend.split(",")]:
+            # an extend chunk of qe new tokens: the last qe positions of each
+            # request's cache, with query rows of the generator's scale
+            gen = torch.Generator(device=dev).manual_seed(1000 + qe)
+            qx = (torch.randn((wl.batch * qe, wl.num_q_heads, wl.head_dim), generator=gen, device=dev)
+                  ).to(torch.float16)
+            ec = B.VerifyCall(qx, x.k_pages, x.v_pages, page_table, kv_lens, qe, x.max_kv_len, x.k_scales,
+                              x.v_scales, x.sm_scale, 0)
+            for _ in range(3):
+                ec.run(stream)
+            us = float(np.median(timed(lambda: ec.run(stream), n_part)))
+            # QK^T and PV: 2 * 2 * D flops per (row, head, visible key)
+            keys = sum(qe * (n - qe) + qe * (qe + 1) // 2 for n in x.kv_lens.tolist())
+            flops = 4 * wl.head_dim * wl.num_q_heads * keys
+            eb = W.verify_algorithmic_bytes(x.kv_lens.tolist(), qe, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                            wl.page_size, wl.kv_dtype)
+            tf = flops / (us * 1e-6) / 1e12
+            ext.append({"q_len": qe, "us_median": round(us, 2), "flops": flops, "TFLOPs": round(tf, 1),
+                        "frac_mfma_fp16": round(tf / PEAK_MFMA_FP16_TFLOPS, 4), "algorithmic_bytes": eb,
+                        "GBps": round(eb / (us * 1e-6) / 1e9, 1), "splits": ec.splits, "chunk_tokens": ec.chunk,
+                        "flags": int(ec.flags.item())})
+            log(f"[bench] extend {qe}: {us:.2f} us, {tf:.1f} TFLOP/s ({100 * tf / PEAK_MFMA_FP16_TFLOPS:.1f}% of "
+                f"fp16 MFMA), {eb / (us * 1e-6) / 1e9:.1f} GB/s, splits {ec.splits}")
+            del ec, qx
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, wl)
@@ -349,6 +381,7 @@ def main():
         "rejection_accept": stoch,
         "topk_candidates": topk,
         "window_verify": win,
+        "extend_chunks": ext,
     }
     print(json.dumps(res), flush=True)
 

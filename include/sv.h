@@ -63,6 +63,11 @@ typedef enum { SV_KV_FP16 = 0, SV_KV_FP8_E4M3 = 1 } sv_kv_dtype;
  * in the paged cache and kv_lens counts them: row i of request b attends to
  * cache positions 0 .. kv_lens[b] - q_len + i.
  *
+ * The same call serves an extend chunk: up to 512 new tokens processed on
+ * top of a cached prefix, a short prefill after it (the glossary at the end
+ * of the page "DFlash -> dLLM self-spec, part 1"); its rows attend causally
+ * exactly as a verify block's do, so q_len may exceed the block sizes 8 and 16.
+ *
  * Sink + sliding window (window > 0; the opt-in sparse mode of the PocketLLM
  * page, "Implemented execution path" and "Validated performance"): row i at
  * position p = kv_lens[b] - q_len + i attends only to the positions t <= p
@@ -72,9 +77,9 @@ typedef enum { SV_KV_FP16 = 0, SV_KV_FP8_E4M3 = 1 } sv_kv_dtype;
  */
 typedef struct {
   int32_t batch;             /* B >= 1 requests */
-  int32_t q_len;             /* verify rows per request, 1..16 */
+  int32_t q_len;             /* rows per request, 1..512 (a verify block, or an extend chunk) */
   int32_t num_q_heads;       /* Hq; query head h uses KV head h / (Hq/Hkv) */
-  int32_t num_kv_heads;      /* Hkv, divides Hq; q_len * Hq/Hkv <= 96 */
+  int32_t num_kv_heads;      /* Hkv, divides Hq; q_len * Hq/Hkv <= 8192 */
   int32_t head_dim;          /* D, must be 256 */
   int32_t page_size;         /* P tokens per page: a multiple of 16, at most 4096 */
   int32_t num_pages;         /* pages in the pool (bounds page ids) */

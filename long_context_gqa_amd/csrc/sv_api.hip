@@ -68,8 +68,8 @@ constexpr int kGroupsPerCU = 1;        // workgroups per CU the automatic plan a
 sv_status validate(const sv_verify_params* p) {
   if (!p) return fail(SV_ERR_INVALID_ARGUMENT, "params is NULL");
   if (p->batch < 1) return fail(SV_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", p->batch);
-  if (p->q_len < 1 || p->q_len > 16)
-    return fail(SV_ERR_UNSUPPORTED, "q_len must be in 1..16 (got %d)", p->q_len);
+  if (p->q_len < 1 || p->q_len > sv::kMaxQLen)
+    return fail(SV_ERR_UNSUPPORTED, "q_len must be in 1..%d (got %d)", sv::kMaxQLen, p->q_len);
   if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
     return fail(SV_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 p->num_q_heads, p->num_kv_heads);
@@ -107,14 +107,10 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   const int G = p->num_q_heads / p->num_kv_heads;
   const int R = p->q_len * G;
   const int rbt = (R + 15) / 16;
-  if (rbt <= 3) {
-    pl->row_blocks = 1;
-    pl->rb = rbt;
-  } else {
-    // more than 48 rows: two workgroups of up to 48 rows read the same keys
-    pl->row_blocks = 2;
-    pl->rb = (rbt + 1) / 2;
-  }
+  // more than 48 rows: several workgroups of up to 48 rows (3 row blocks of
+  // 16) read the same keys, the rows dealt out evenly
+  pl->row_blocks = (rbt + 2) / 3;
+  pl->rb = (rbt + pl->row_blocks - 1) / pl->row_blocks;
   // positions the chunks tile: the whole context, or with a sliding window
   // at most the sink, the window and the block (plus 16-token alignment)
   long long maxkv = p->max_kv_len;
@@ -143,6 +139,15 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     if (chunk < kMinChunk) chunk = kMinChunk;
     S = (maxkv + chunk - 1) / chunk;
     if (S < 1) S = 1;
+    if (rgs > 1) {
+      // the row tiles of a unit all run on the unit's XCD (unit mod 8), so a
+      // unit count that is a multiple of 8 spreads the work over every XCD
+      const long long hb = (long long)p->batch * p->num_kv_heads;
+      long long need = 8;
+      while (need > 1 && hb % (8 / need * 2) == 0) need /= 2;  // 8 / gcd(8, hb)
+      const long long S8 = (S + need - 1) / need * need;
+      if (maxkv >= S8 * kMinChunk) S = S8;
+    }
   }
   long long chunk = (maxkv + S - 1) / S;
   chunk = (chunk + 63) / 64 * 64;

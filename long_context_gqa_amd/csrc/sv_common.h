@@ -15,7 +15,8 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWave * kWavesPerGroup;
 constexpr int kStep = 16;        // tokens per wave step (one MFMA M/K block)
-constexpr int kMaxRows = 96;     // q_len * (Hq/Hkv) per KV head
+constexpr int kMaxQLen = 512;    // rows per request: a verify block, or an extend chunk after a prefix
+constexpr int kMaxRows = 8192;   // q_len * (Hq/Hkv) per KV head
 constexpr int kRowStride = kHeadDim + 4;  // fp32 LDS row stride of the combine buffer
 
 // Arguments of the verify-attention kernel (passed by value).
@@ -35,7 +36,7 @@ struct AttnArgs {
   int32_t* flags;
   int32_t batch, q_len, num_q_heads, num_kv_heads, group, page_size;
   int32_t num_pages, max_pages, max_kv_len, chunk, num_splits;
-  int32_t row_blocks;  // workgroups per (chunk, KV head, request): 1, or 2 for > 48 rows
+  int32_t row_blocks;  // workgroups per (chunk, KV head, request), each of up to 48 rows
   int32_t units;       // num_splits * num_kv_heads * batch, numbered split-major
   int32_t window, sink;  // sliding window (0: full attention) and leading sink positions
   float scale_log2;  // sm_scale * log2(e)

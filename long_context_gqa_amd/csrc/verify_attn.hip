@@ -707,16 +707,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int ts = wave;
-  // Workgroup -> (key chunk, KV head, request, row block). With two row
-  // blocks the pair that shares a (chunk, KV head, request) gets ids 8 apart
-  // in the same group of 16, i.e. the same XCD at about the same time (ids
-  // go round-robin over the 8 XCDs), so the second reader of each K/V byte
-  // mostly finds it in that XCD's L2.
+  // Workgroup -> (key chunk, KV head, request, row tile). With n row tiles
+  // the n workgroups that share a (chunk, KV head, request) get ids 8 apart
+  // in one group of 8n, i.e. the same XCD at about the same time (ids go
+  // round-robin over the 8 XCDs), so the later readers of each K/V byte
+  // mostly find it in that XCD's L2.
   int unit = blockIdx.x, rblk = 0;
-  if (a.row_blocks == 2) {
+  if (a.row_blocks > 1) {
     const int r = blockIdx.x >> 3;
-    rblk = r & 1;
-    unit = ((r >> 1) << 3) | (blockIdx.x & 7);
+    rblk = r % a.row_blocks;
+    unit = ((r / a.row_blocks) << 3) | (blockIdx.x & 7);
     if (unit >= a.units) return;
   }
   // Units are numbered split-major: every (KV head, request) of chunk 0,
@@ -739,7 +739,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     }
   }
   const int G = a.group, R = q_len * G, Hq = a.num_q_heads;
-  if (row0 >= R) return;  // a narrow block leaves the second row block empty
+  if (row0 >= R) return;  // a narrow block leaves the last row tiles empty
   const size_t split_stride = (size_t)a.batch * a.q_len * Hq;  // rows of one split's partials
 
   const int raw_kv = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
@@ -1127,10 +1127,12 @@ void launch_rb(const AttnArgs& a, int rb, dim3 grid, hipStream_t s) {
 
 template <bool FP8, bool WIN>
 void launch_depth(const AttnArgs& a, int rb, hipStream_t s) {
-  // one workgroup per unit; with two row blocks, 16 ids per 8 units, and the
-  // two workgroups on the same keys (rb is then 2 or 3) keep two steps in flight
-  if (a.row_blocks == 2) launch_rb<FP8, 2, WIN>(a, rb, dim3(2 * ((a.units + 7) / 8 * 8)), s);
-  else launch_rb<FP8, 1, WIN>(a, rb, dim3(a.units), s);
+  // one workgroup per unit; with n row tiles, 8n ids per 8 units, and the
+  // workgroups on the same keys (rb is then 2 or 3) keep two steps in flight
+  if (a.row_blocks > 1)
+    launch_rb<FP8, 2, WIN>(a, rb, dim3(a.row_blocks * ((a.units + 7) / 8 * 8)), s);
+  else
+    launch_rb<FP8, 1, WIN>(a, rb, dim3(a.units), s);
 }
 
 void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s) {

@@ -47,13 +47,13 @@ def _p(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q_len=0), B.SV_ERR_UNSUPPORTED),
-    (dict(q_len=17), B.SV_ERR_UNSUPPORTED),
+    (dict(q_len=513, max_kv_len=4104), B.SV_ERR_UNSUPPORTED),
     (dict(head_dim=128), B.SV_ERR_UNSUPPORTED),
     (dict(num_q_heads=25), B.SV_ERR_INVALID_ARGUMENT),
     (dict(page_size=24), B.SV_ERR_UNSUPPORTED),
     (dict(max_kv_len=7), B.SV_ERR_INVALID_ARGUMENT),
     (dict(max_kv_len=5000), B.SV_ERR_INVALID_ARGUMENT),  # beyond max_pages_per_req * page_size
-    (dict(num_q_heads=48, num_kv_heads=2, q_len=8), B.SV_ERR_UNSUPPORTED),  # 192 rows per KV head
+    (dict(num_q_heads=64, num_kv_heads=2, q_len=257), B.SV_ERR_UNSUPPORTED),  # 8224 rows per KV head
     (dict(batch=0), B.SV_ERR_INVALID_ARGUMENT),
 ])
 def test_plan_rejects_bad_shapes(kw, status):
@@ -61,6 +61,16 @@ def test_plan_rejects_bad_shapes(kw, status):
         B.sv_verify_plan(_p(**kw))
     assert e.value.status == status
     assert B.sv_verify_workspace_bytes(_p(**kw)) == 0
+
+
+def test_plan_accepts_extend_chunks_up_to_the_limits():
+    # an extend chunk of 512 rows, and 8192 rows on one KV head (the maxima)
+    for kw in (dict(q_len=512), dict(q_len=512, num_q_heads=16, num_kv_heads=1), dict(q_len=100)):
+        p = _p(**kw)
+        s, c = B.sv_verify_plan(p)
+        assert s >= 1 and c % 64 == 0
+        rows = p.batch * p.q_len * p.num_q_heads
+        assert B.sv_verify_workspace_bytes(p) >= (0 if s == 1 else s * rows * 256 * 4)
 
 
 def test_plan_chunks_are_anchored_multiples_of_64():
@@ -123,7 +133,7 @@ def test_block_entry_points_reject_bad_arguments_without_launch():
     st = lib.sv_verify_attention_ragged(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, fake,
                                         None, fake, 16, None, None)
     assert st == B.SV_ERR_WORKSPACE_TOO_SMALL
-    st = lib.sv_verify_attention_ragged(ctypes.byref(_p(q_len=17)), fake, fake, fake, fake, None, None, fake,
+    st = lib.sv_verify_attention_ragged(ctypes.byref(_p(q_len=513)), fake, fake, fake, fake, None, None, fake,
                                         fake, fake, None, fake, 1 << 30, None, None)
     assert st == B.SV_ERR_UNSUPPORTED
     # ragged accept: q_start and (for widths > 1) block_ids are required
