@@ -153,27 +153,33 @@ __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& w
   }
 }
 
-// Scores of one fp16 step and the fp16 P^T fragments.
-template <int RB, bool WIN>
-__device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __restrict__ qf,
-                                            WaveState<RB>& ws, half4_t (&pb)[RB], int lane, int t0,
-                                            const RowMask<RB, WIN>& mk, float scale_log2) {
-  float x[RB][4];
+// The scaled scores of one fp16 step: per row block, the 8 k-steps of the
+// score matrix ops on the K fragments and the wave's Q fragments (held in
+// registers for the whole loop), in two independent chains.
+template <int RB>
+__device__ __forceinline__ void scores_mfma(const KFrag& kf, const u32x4 (&qa)[RB][8], float scale_log2,
+                                            float (&x)[RB][4]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    // Q is re-read from LDS every step; the opaque offset keeps the compiler
-    // from hoisting 32*RB registers of fragments out of the loop.
-    int qo = rb * 8 * kWave + lane;
-    asm volatile("" : "+v"(qo));
-    u32x4 qv[8];
+    floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma_16x16x32(kf.k[s], qv[s], acc);
+    for (int s = 0; s < 8; s += 2) {
+      a0 = mfma_16x16x32(kf.k[s], qa[rb][s], a0);
+      a1 = mfma_16x16x32(kf.k[s + 1], qa[rb][s + 1], a1);
+    }
+    const floatx4 acc = a0 + a1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[rb][i] = acc[i] * scale_log2;
   }
+}
+
+// Scores of one fp16 step and the fp16 P^T fragments.
+template <int RB, bool WIN>
+__device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4 (&qa)[RB][8], WaveState<RB>& ws,
+                                            half4_t (&pb)[RB], int lane, int t0, const RowMask<RB, WIN>& mk,
+                                            float scale_log2) {
+  float x[RB][4];
+  scores_mfma<RB>(kf, qa, scale_log2, x);
   float p[RB][4];
   softmax_step<RB>(x, ws, p, lane, t0, mk);
 #pragma unroll
@@ -184,8 +190,7 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4* __rest
 // The pieces of one step for the software-pipelined fp16 loop, where the PV
 // matrix ops of step k are issued right after the score matrix ops of step
 // k+1, and the softmax of k+1 fills their shadow:
-//   scores_mfma   the scaled scores of step k+1 (Q read from LDS with one
-//                 wait per row block);
+//   scores_mfma   the scaled scores of step k+1 (Q fragments in registers);
 //   mask_check    causal/tail masking without branches (per-row limits are
 //                 computed once), each lane's own max, and whether any lane
 //                 needs its row's reference moved;
@@ -293,47 +298,6 @@ __device__ __forceinline__ float half_at(const u32x4 (&h)[2], int idx) {
   const uint32_t w = h[idx >> 3][(idx >> 1) & 3];
   const uint16_t bits = (idx & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFFu);
   return (float)__builtin_bit_cast(_Float16, bits);
-}
-
-// Scores of one FP8 step: per 64-channel block, two MFMAs on the converted
-// K, then S = sum_b scale_b * partial_b.
-template <int RB, bool WIN>
-__device__ __forceinline__ void step_scores8(const KFrag8& kf, const u32x4* __restrict__ qf,
-                                             WaveState<RB>& ws, float (&p)[RB][4], int lane, int t0,
-                                             const RowMask<RB, WIN>& mk, float scale_log2) {
-  u32x4 kc[8];
-#pragma unroll
-  for (int bk = 0; bk < 4; ++bk) {
-    kc[2 * bk] = u32x4{e4m3x2_lo(kf.k[bk][0]), e4m3x2_hi(kf.k[bk][0]), e4m3x2_lo(kf.k[bk][1]),
-                       e4m3x2_hi(kf.k[bk][1])};
-    kc[2 * bk + 1] = u32x4{e4m3x2_lo(kf.k[bk][2]), e4m3x2_hi(kf.k[bk][2]), e4m3x2_lo(kf.k[bk][3]),
-                           e4m3x2_hi(kf.k[bk][3])};
-  }
-  float fk[4][4];  // [token i][block]
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * scale_log2;
-  float x[RB][4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    int qo = rb * 8 * kWave + lane;
-    asm volatile("" : "+v"(qo));
-    u32x4 qv[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qv[s] = qf[qo + s * kWave];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[rb][i] = 0.f;
-#pragma unroll
-    for (int bk = 0; bk < 4; ++bk) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_16x16x32(kc[2 * bk], qv[2 * bk], acc);
-      acc = mfma_16x16x32(kc[2 * bk + 1], qv[2 * bk + 1], acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[rb][i] += fk[i][bk] * acc[i];
-    }
-  }
-  softmax_step<RB>(x, ws, p, lane, t0, mk);
 }
 
 // O^T += V^T . P^T for one FP8 step: MFMA block j = 4*bb + c holds channels
@@ -609,38 +573,13 @@ __device__ __forceinline__ void ring_read_v8(VFrag8& f, uint32_t addr) {
       : "memory");
 }
 
+// The scaled scores of one FP8 step: per 64-channel block, two matrix ops
+// on the converted K and the wave's Q fragments (in registers), one
+// accumulator per (row block, scale block) so the block scales are applied
+// after all matrix ops are issued: S = sum_b scale_b * partial_b.
 template <int RB>
-__device__ __forceinline__ void scores_mfma(const KFrag& kf, const u32x4* __restrict__ qf, int lane,
-                                            float scale_log2, float (&x)[RB][4]) {
-  const uint32_t q_lds = lds_addr(qf);
-  floatx4 acc[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    // the row block's 8 Q fragments (1 KB apart in LDS) with one wait, then
-    // two independent chains of four (even and odd k-steps)
-    u32x4 qv[8];
-    ring_read8<63, false, 1024>(qv, q_lds + (uint32_t)(rb * 8 * kWave + lane) * 16u);
-    floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 8; s += 2) {
-      a0 = mfma_16x16x32(kf.k[s], qv[s], a0);
-      a1 = mfma_16x16x32(kf.k[s + 1], qv[s + 1], a1);
-    }
-    acc[rb] = a0 + a1;
-  }
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[rb][i] = acc[rb][i] * scale_log2;
-}
-
-// The scaled scores of one FP8 step (the matrix ops and block scales of
-// step_scores8, without the softmax), for the pipelined loop: Q read with
-// one wait per row block, one accumulator per (row block, scale block) so
-// the block scales are applied after all matrix ops are issued.
-template <int RB>
-__device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4* __restrict__ qf, int lane,
-                                             float scale_log2, float (&x)[RB][4]) {
+__device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4 (&qa)[RB][8], float scale_log2,
+                                             float (&x)[RB][4]) {
   u32x4 kc[8];
 #pragma unroll
   for (int bk = 0; bk < 4; ++bk) {
@@ -649,16 +588,13 @@ __device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4* __re
     kc[2 * bk + 1] = u32x4{e4m3x2_lo(kf.k[bk][2]), e4m3x2_hi(kf.k[bk][2]), e4m3x2_lo(kf.k[bk][3]),
                            e4m3x2_hi(kf.k[bk][3])};
   }
-  const uint32_t q_lds = lds_addr(qf);
   floatx4 acc[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    u32x4 qv[8];
-    ring_read8<63, false, 1024>(qv, q_lds + (uint32_t)(rb * 8 * kWave + lane) * 16u);
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
-      acc[rb][bk] = mfma_16x16x32(kc[2 * bk], qv[2 * bk], floatx4{0.f, 0.f, 0.f, 0.f});
-      acc[rb][bk] = mfma_16x16x32(kc[2 * bk + 1], qv[2 * bk + 1], acc[rb][bk]);
+      acc[rb][bk] = mfma_16x16x32(kc[2 * bk], qa[rb][2 * bk], floatx4{0.f, 0.f, 0.f, 0.f});
+      acc[rb][bk] = mfma_16x16x32(kc[2 * bk + 1], qa[rb][2 * bk + 1], acc[rb][bk]);
     }
   }
   float fk[4][4];  // [token i][block]
@@ -862,6 +798,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     // scale sets (5 operations) and V bytes (4 operations): the V half-step
     // (4) is newer than a K read, the next K half-step (5) than a V read)
     const uint32_t ring_lds = lds_addr(ring);
+    u32x4 qa[RB][8];  // the wave's Q fragments, in registers for the whole loop
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      ring_read8<63, false, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const int pid = bstart == 0 ? pid_first : page_ids(bstart);
       const int nb = min(kWave, my_steps - bstart);
@@ -893,7 +833,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         KFrag8 kf;
         ring_read_k8<kWaitK>(kf, sbase(0) + k8_lane_off(lane), sbase(0) + 8192 + 32 * (lane >> 4));
         issue_k(min(DEPTH, nb - 1), 0);
-        step_scores8<RB>(kf, qf, ws, pr, lane, step_t0(0), mk, a.scale_log2);
+        float x0[RB][4];
+        scores8_mfma<RB>(kf, qa, a.scale_log2, x0);
+        softmax_step<RB>(x0, ws, pr, lane, step_t0(0), mk);
         sv[0] = kf.sv[0];
         sv[1] = kf.sv[1];
       }
@@ -906,7 +848,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         ring_read_k8<kWaitK>(kf, sbase(kk + 1) + k8_lane_off(lane), sbase(kk + 1) + 8192 + 32 * (lane >> 4));
         issue_k(min(kk + 1 + DEPTH, nb - 1), (kk + 1) & (DEPTH - 1));
         float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
-        scores8_mfma<RB>(kf, qf, lane, a.scale_log2, x);
+        scores8_mfma<RB>(kf, qa, a.scale_log2, x);
         // (a step before the wave's last of the batch ends below kv_len)
         step_pv8<RB, false>(vf, sv, pr, ws, lane, t0, kv);
         sv[0] = kf.sv[0];
@@ -932,6 +874,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     }
   } else {
     // ---- each wave owns its token steps and a private one-step LDS ring ----
+    // The wave's Q fragments stay in registers for the whole loop (32 per
+    // row block): re-reading them from LDS at every step made up 24 of the
+    // step's 40 KB of LDS reads.
+    u32x4 qa[RB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      ring_read8<63, false, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const int pid = bstart == 0 ? pid_first : page_ids(bstart);
       const int nb = min(kWave, my_steps - bstart);
@@ -962,7 +911,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         KFrag kf;
         ring_read8<kWait, false, 64>(kf.k, ring_lds + stage(0) + k_lane_off(lane));
         dma_k<0, 8>(step_base(min(DEPTH, nb - 1), kpool), ring + stage(0), lane);
-        step_scores<RB>(kf, qf, ws, pb, lane, step_t0(0), mk, a.scale_log2);
+        step_scores<RB>(kf, qa, ws, pb, lane, step_t0(0), mk, a.scale_log2);
       }
       for (int kk = 0; kk + 1 < nb; ++kk) {
         const int t0 = step_t0(kk);
@@ -974,7 +923,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         ring_read8_acc<kWait, 64>(kf.k, ring_lds + st1 + k_lane_off(lane));
         dma_k<0, 8>(step_base(min(kk + 1 + DEPTH, nb - 1), kpool), ring + st1, lane);
         float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
-        scores_mfma<RB>(kf, qf, lane, a.scale_log2, x);
+        scores_mfma<RB>(kf, qa, a.scale_log2, x);
         // (a step before the wave's last of the batch ends below kv_len)
         step_pv<RB, false>(vf, pb, ws, lane, t0, kv);
         const bool any = mask_check<RB>(x, lmx, ws, mk, lane, step_t0(kk + 1));
