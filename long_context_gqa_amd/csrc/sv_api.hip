@@ -82,6 +82,8 @@ sv_status validate(const sv_verify_params* p) {
   if (p->page_size < 16 || p->page_size % 16 != 0 || p->page_size > 4096)
     return fail(SV_ERR_UNSUPPORTED, "page_size must be a multiple of 16 in 16..4096 (got %d)", p->page_size);
   if (p->num_pages < 1) return fail(SV_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  if ((long long)p->num_pages * p->num_kv_heads * p->page_size > 0xffffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "num_pages * num_kv_heads * page_size must be below 2^32 (cache rows)");
   if (p->max_pages_per_req < 1) return fail(SV_ERR_INVALID_ARGUMENT, "max_pages_per_req must be >= 1");
   if (p->max_kv_len < p->q_len)
     return fail(SV_ERR_INVALID_ARGUMENT, "max_kv_len (%d) must be >= q_len (%d)", p->max_kv_len, p->q_len);

@@ -709,36 +709,39 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
   // page id of each of the wave's steps bstart .. bstart+63, one per lane
-  auto page_ids = [&](int bstart) {
-    int pid = 0;
+  // Lane kl of the wave finds the cache row ((page, KV head, slot); the pool
+  // holds fewer than 2^32 rows) of the first token of the wave's step
+  // bstart + kl, once per batch of 64 steps; a step's DMAs then take it with
+  // one readlane.
+  auto step_rows = [&](int bstart) {
+    uint32_t row = 0;
     const int kl = bstart + lane;
     if (kl < my_steps) {
       const int t = live_t0(ts + kl * NTS);
-      pid = ptab[t / P];
+      int pid = ptab[t / P];
       if (pid < 0 || pid >= a.num_pages) {
         flag_bits |= 0x4;
         pid = 0;
       }
+      row = ((uint32_t)pid * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
     }
-    return pid;
+    return row;
   };
-  // (page, KV head, slot) row of the first token of the wave's step bstart + kk
-  auto tok_row = [&](int pid, int bstart, int kk) {
-    const int pg = __builtin_amdgcn_readlane(pid, kk);
-    return ((size_t)pg * Hkv + g) * P + (live_t0(ts + (bstart + kk) * NTS) % P);
+  auto tok_row = [&](uint32_t rows, int kk) {
+    return (size_t)(uint32_t)__builtin_amdgcn_readlane((int)rows, kk);
   };
   constexpr int kStageBytes = FP8 ? kStage8 : kRingStage;
   char* const ring = reinterpret_cast<char*>(bigsm) + wave * DEPTH * kStageBytes;
   // The first steps' DMAs go out before Q is staged, so the two latencies
   // overlap (Q lives in its own array; the ring is the wave's own). Step
   // indices past the batch are clamped to its last step.
-  int pid_first = 0;
+  uint32_t rows_first = 0;
   if (my_steps > 0) {
-    pid_first = page_ids(0);
+    rows_first = step_rows(0);
     const int nb0 = min(kWave, my_steps);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      const size_t tr = tok_row(pid_first, 0, min(d, nb0 - 1));
+      const size_t tr = tok_row(rows_first, min(d, nb0 - 1));
       char* stage = ring + d * kStageBytes;
       if constexpr (FP8) {
         dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, stage, lane);
@@ -803,15 +806,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     for (int rb = 0; rb < RB; ++rb)
       ring_read8<63, false, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
-      const int pid = bstart == 0 ? pid_first : page_ids(bstart);
+      const uint32_t rows = bstart == 0 ? rows_first : step_rows(bstart);
       const int nb = min(kWave, my_steps - bstart);
       auto step_t0 = [&](int kk) { return live_t0(ts + (bstart + kk) * NTS); };
       auto issue_k = [&](int kk, int stg) {
-        const size_t tr = tok_row(pid, bstart, kk);
+        const size_t tr = tok_row(rows, kk);
         dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring + stg * kStage8, lane);
       };
       auto issue_v = [&](int kk, int stg) {
-        dma_v8(vpool8 + tok_row(pid, bstart, kk) * kHeadDim, ring + stg * kStage8, lane);
+        dma_v8(vpool8 + tok_row(rows, kk) * kHeadDim, ring + stg * kStage8, lane);
       };
       if (bstart > 0) {  // (the first batch's first steps were issued before Q staging)
 #pragma unroll
@@ -882,10 +885,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     for (int rb = 0; rb < RB; ++rb)
       ring_read8<63, false, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
-      const int pid = bstart == 0 ? pid_first : page_ids(bstart);
+      const uint32_t rows = bstart == 0 ? rows_first : step_rows(bstart);
       const int nb = min(kWave, my_steps - bstart);
       auto step_t0 = [&](int kk) { return live_t0(ts + (bstart + kk) * NTS); };
-      auto step_base = [&](int kk, const _Float16* pool) { return pool + tok_row(pid, bstart, kk) * kHeadDim; };
+      auto step_base = [&](int kk, const _Float16* pool) { return pool + tok_row(rows, kk) * kHeadDim; };
       // DEPTH steps in flight per wave in its ring, one in registers. Order
       // of DMA issue: K(k+DEPTH) right after K(k) is read, V(k+DEPTH) right
       // after V(k) is read, so before reading a half-step exactly 2*DEPTH-1

@@ -55,6 +55,7 @@ def _p(**kw):
     (dict(max_kv_len=5000), B.SV_ERR_INVALID_ARGUMENT),  # beyond max_pages_per_req * page_size
     (dict(num_q_heads=64, num_kv_heads=2, q_len=257), B.SV_ERR_UNSUPPORTED),  # 8224 rows per KV head
     (dict(batch=0), B.SV_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=1 << 27), B.SV_ERR_UNSUPPORTED),  # 2^33 cache rows: beyond 32-bit row indices
 ])
 def test_plan_rejects_bad_shapes(kw, status):
     with pytest.raises(B.SvError) as e:
