@@ -34,6 +34,7 @@
 namespace sv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -47,7 +48,6 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b,
 
 __device__ __forceinline__ floatx4 mfma_16x16x16(uint32_t a0, uint32_t a1, const half4_t& b,
                                                  floatx4 c) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   u32x2 av = {a0, a1};
   return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), b, c, 0, 0, 0);
 }
@@ -59,7 +59,7 @@ struct KFrag {
   u32x4 k[8];  // k[s]: token lane%16, channels 32s + 8*(lane/16) .. +8
 };
 struct VFrag {
-  u32x4 v[8];  // v[2e+h]: token 4*(lane/16)+e, channels 128h + 8*(lane%16) .. +8
+  u32x2 v[16];  // v[cb]: channel 16cb + lane%16 of tokens 4*(lane/16) + 0..3 (the PV A operand)
 };
 
 // Multiply one accumulator tuple by a per-lane factor in place. Done in
@@ -348,38 +348,27 @@ __device__ __forceinline__ void step_pv8(VFrag8& vf, const u32x4 (&sv)[2], const
   }
 }
 
-// O^T += V^T . P^T for one step.
+// O^T += V^T . P^T for one step: matrix op cb covers channels 16cb..16cb+15,
+// and its accumulator holds channels 16cb + 4*(lane/16) + i of row lane%16.
 template <int RB, bool MASK = true>
 __device__ __forceinline__ void step_pv(VFrag& vf, const half4_t (&pb)[RB], WaveState<RB>& ws,
                                         int lane, int t0, int kv) {
-  const int hi = lane >> 4;
   // Keys at or past kv_len may be poison in the page's unused slots; their
-  // weight is exactly 0 but 0 * NaN is NaN, so clear those V rows.
+  // weight is exactly 0 but 0 * NaN is NaN, so clear those V values.
   if (MASK && t0 + kStep > kv) {
+    const int tok = t0 + 4 * (lane >> 4);
+    const uint32_t m0 = (tok + 0 < kv ? 0x0000ffffu : 0u) | (tok + 1 < kv ? 0xffff0000u : 0u);
+    const uint32_t m1 = (tok + 2 < kv ? 0x0000ffffu : 0u) | (tok + 3 < kv ? 0xffff0000u : 0u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (t0 + 4 * hi + e >= kv) {
-        vf.v[2 * e] = u32x4{0u, 0u, 0u, 0u};
-        vf.v[2 * e + 1] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int cb = 0; cb < 16; ++cb) {
+      vf.v[cb].x &= m0;
+      vf.v[cb].y &= m1;
     }
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-      const uint32_t w0 = vf.v[h][c2], w1 = vf.v[2 + h][c2];
-      const uint32_t w2 = vf.v[4 + h][c2], w3 = vf.v[6 + h][c2];
-      const uint32_t lo0 = (w0 & 0xffffu) | (w1 << 16), lo1 = (w2 & 0xffffu) | (w3 << 16);
-      const uint32_t hi0 = (w0 >> 16) | (w1 & 0xffff0000u), hi1 = (w2 >> 16) | (w3 & 0xffff0000u);
-      const int j = 8 * h + 2 * c2;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        ws.o[rb][j] = mfma_16x16x16(lo0, lo1, pb[rb], ws.o[rb][j]);
-        ws.o[rb][j + 1] = mfma_16x16x16(hi0, hi1, pb[rb], ws.o[rb][j + 1]);
-      }
-    }
-  }
+    for (int rb = 0; rb < RB; ++rb) ws.o[rb][cb] = mfma_16x16x16(vf.v[cb].x, vf.v[cb].y, pb[rb], ws.o[rb][cb]);
 }
 
 }  // namespace
@@ -458,8 +447,11 @@ __device__ __forceinline__ void dma_k(const _Float16* kb, char* ring, int lane) 
 template <int B0, int B1>
 __device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) {
 #pragma unroll
-  for (int j = B0; j < B1; ++j)
-    __builtin_amdgcn_global_load_lds(SV_GP(vb + (j * kWave + lane) * 8), SV_LP(ring + j * 1024), 16, 0, 0);
+  for (int j = B0; j < B1; ++j) {
+    const int t = 2 * j + (lane >> 5);
+    const int c = (lane & 31) ^ (2 * (t & 3));
+    __builtin_amdgcn_global_load_lds(SV_GP(vb + t * kHeadDim + 8 * c), SV_LP(ring + j * 1024), 16, 0, 0);
+  }
 }
 // The same read into accumulation registers: for fragments that only feed
 // matrix ops (which read A/B operands from them), keeping them out of the
@@ -483,13 +475,56 @@ __device__ __forceinline__ void ring_read8_acc(u32x4 (&d)[8], uint32_t addr) {
       : "memory");
 }
 // Per-lane ring offsets of the operand reads. K: lane (token l%16, group
-// l/16) reads k-step s at k_lane_off + 64*s. V: fragment 2e+h (token
-// 4*(l/16)+e, channels 128h + 8*(l%16)) at v_lane_off + 256*(2e+h).
+// l/16) reads k-step s at k_lane_off + 64*s.
 __device__ __forceinline__ uint32_t k_lane_off(int lane) {
   const int t = lane & 15, g = lane >> 4;
   return t * 512 + 16 * (g ^ (t & 3));
 }
-__device__ __forceinline__ uint32_t v_lane_off(int lane) { return (lane >> 4) * 2048 + (lane & 15) * 16; }
+
+// V^T fragments of one step by transposing LDS reads. ds_read_b64_tr_b16
+// works on groups of 16 lanes: lane i of a group receives, as its element r,
+// the 16-bit element i%4 of the 8 bytes that lane 4r + i/4 of the group
+// addresses (pinned with a probe on the GPU). Lane 4r + q of group g
+// addresses token 4g + r, channels 16cb + 4q .. +3, so lane i receives
+// channel 16cb + i of tokens 4g + 0..3: the A operand of the PV matrix op.
+// V rows are stored with the 32-byte window of channel block cb of token t at
+// window cb ^ (t & 3) (dma_v), so a group's four rows fall in different
+// banks; window cb ^ r = 4*(cb/4) + ((cb%4) ^ r) gives four per-lane bases
+// (cb%4 = 0..3) and an immediate offset of 128*(cb/4). VMCNT as in
+// ring_read8.
+__device__ __forceinline__ uint32_t v_lane_off(int lane) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  return (4 * g + r) * 512 + 8 * q;
+}
+template <int VMCNT>
+__device__ __forceinline__ void ring_read_vt(VFrag& f, uint32_t addr, int lane) {
+  const uint32_t r32 = 32u * (uint32_t)((lane >> 2) & 3);
+  const uint32_t b0 = addr + (0u ^ r32), b1 = addr + (32u ^ r32), b2 = addr + (64u ^ r32), b3 = addr + (96u ^ r32);
+  asm volatile(
+      "s_waitcnt vmcnt(%20)\n\t"
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %18\n\t"
+      "ds_read_b64_tr_b16 %3, %19\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:128\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:128\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:128\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:256\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:256\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:256\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:256\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:384\n\t"
+      "ds_read_b64_tr_b16 %13, %17 offset:384\n\t"
+      "ds_read_b64_tr_b16 %14, %18 offset:384\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:384\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.v[0]), "=&v"(f.v[1]), "=&v"(f.v[2]), "=&v"(f.v[3]), "=&v"(f.v[4]), "=&v"(f.v[5]),
+        "=&v"(f.v[6]), "=&v"(f.v[7]), "=&v"(f.v[8]), "=&v"(f.v[9]), "=&v"(f.v[10]), "=&v"(f.v[11]),
+        "=&v"(f.v[12]), "=&v"(f.v[13]), "=&v"(f.v[14]), "=&v"(f.v[15])
+      : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "n"(VMCNT)
+      : "memory");
+}
 
 // FP8 ring stage: K bytes (4 KB), V bytes (4 KB), the step's K and V scales
 // (2 x 128 B, padded to 256).
@@ -920,7 +955,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         const int t0 = step_t0(kk);
         const int st = stage(kk), st1 = stage(kk + 1);
         VFrag vf;
-        ring_read8<kWait, false, 256>(vf.v, ring_lds + st + 8192 + v_lane_off(lane));
+        ring_read_vt<kWait>(vf, ring_lds + st + 8192 + v_lane_off(lane), lane);
         dma_v<0, 8>(step_base(min(kk + DEPTH, nb - 1), vpool), ring + st + 8192, lane);
         KFrag kf;
         ring_read8_acc<kWait, 64>(kf.k, ring_lds + st1 + k_lane_off(lane));
@@ -943,7 +978,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       }
       {
         VFrag vf;
-        ring_read8<kWait, false, 256>(vf.v, ring_lds + stage(nb - 1) + 8192 + v_lane_off(lane));
+        ring_read_vt<kWait>(vf, ring_lds + stage(nb - 1) + 8192 + v_lane_off(lane), lane);
         step_pv<RB>(vf, pb, ws, lane, step_t0(nb - 1), kv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -989,7 +1024,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       for (int rb = 0; rb < RB; ++rb) {
         float* rowp = obuf + (rowbase + rb * 16 + lo) * kRowStride;
         // O^T block j of lane (hi, lo) holds channel rows 4*hi + i of row lo:
-        // fp16 KV block j = 8h + c is channels 128h + 8*(4*hi+i) + c;
+        // fp16 KV block j is channels 16j + 4*hi + i;
         // FP8 KV block j = 4bb + c is channels 64bb + 4*(4*hi+i) + c
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -1006,12 +1041,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
               d0p = rowp + 64 * (2 * h) + 16 * hi + 4 * i;
               d1p = rowp + 64 * (2 * h + 1) + 16 * hi + 4 * i;
             } else {
-              v0 = make_float4(ws.o[rb][8 * h + 0][i], ws.o[rb][8 * h + 1][i], ws.o[rb][8 * h + 2][i],
-                               ws.o[rb][8 * h + 3][i]);
-              v1 = make_float4(ws.o[rb][8 * h + 4][i], ws.o[rb][8 * h + 5][i], ws.o[rb][8 * h + 6][i],
-                               ws.o[rb][8 * h + 7][i]);
-              d0p = rowp + 128 * h + 32 * hi + 8 * i;
-              d1p = d0p + 4;
+              // blocks j = 8h + 2i and 8h + 2i + 1
+              const int j0 = 8 * h + 2 * i;
+              v0 = make_float4(ws.o[rb][j0][0], ws.o[rb][j0][1], ws.o[rb][j0][2], ws.o[rb][j0][3]);
+              v1 = make_float4(ws.o[rb][j0 + 1][0], ws.o[rb][j0 + 1][1], ws.o[rb][j0 + 1][2], ws.o[rb][j0 + 1][3]);
+              d0p = rowp + 16 * j0 + 4 * hi;
+              d1p = d0p + 16;
             }
             float4* q0 = reinterpret_cast<float4*>(d0p);
             float4* q1 = reinterpret_cast<float4*>(d1p);
