@@ -1,34 +1,37 @@
-// Paged causal GQA of a speculative verify block on gfx950 (fp16 KV).
+// Paged causal GQA of a speculative verify block on gfx950 (fp16 or FP8 KV).
 //
-// One workgroup owns one (key chunk, KV head, request). All q_len x G rows of
-// the KV head's query group ("packed rows": the verify positions folded with
-// the G query heads that share the KV head) are processed together, so every
-// K/V byte read from HBM is used by every row of the group in registers.
+// One workgroup owns one (key chunk, KV head, request, row tile). All q_len x G
+// rows of the KV head's query group ("packed rows": the verify positions
+// folded with the G query heads that share the KV head) are processed
+// together, so every K/V byte read from HBM is used by every row of the group
+// in registers.
 //
 // Matrix-core mapping (wave64, v_mfma 16x16):
 //   S^T = K . Q^T   with 16x16x32 f16: M = 16 tokens, N = 16 rows, K = 32 channels.
 //                    A = K rows loaded straight from the page (lane = token),
-//                    B = Q fragments kept in LDS for the whole chunk.
+//                    B = Q fragments, loaded once into each wave's registers.
 //   O^T = V^T . P^T with 16x16x16 f16: M = 16 channels, N = 16 rows, K = 16 tokens.
 //                    B = P^T is the S^T accumulator converted in place: the
 //                    lane that holds a row's scores also holds its softmax
 //                    state and its O accumulators, so the online-softmax
 //                    rescale needs no cross-lane traffic.
-//                    A = V^T is built from 16-byte row loads of V with a 2x2
-//                    half-word transpose (channel d of block j is
-//                    128*(j/8) + 8*lane16 + j%8).
+//                    A = V^T: for fp16 KV read from LDS by the transposing
+//                    ds_read_b64_tr_b16 (block j is channels 16j .. 16j+15);
+//                    for FP8 KV interleaved bytewise in registers and
+//                    converted (block j = 4bb + c is channels
+//                    64bb + 4*lane16 + c).
 // The reduction order inside one MFMA is the hardware's; only the pairing of
 // A and B slots is relied on, plus the accumulator layout
 // (lane l holds rows 4*(l/16)+i, column l%16).
 //
 // The chunk's 16-token steps are dealt round-robin to the 4 waves of the
-// workgroup. Each wave keeps one step of K/V in flight while it computes the
-// previous one. At the end the waves' (m, l, O) are combined through LDS and
-// the workgroup writes either the final fp16 rows (request fits one chunk)
-// or an fp32 partial (o normalised, lse) for the merge kernel. A workgroup
-// holds at most 48 rows; a KV head with more (up to 96) is covered by two
-// workgroups that read the same keys, placed on the same XCD so that the
-// second read is mostly served by its L2.
+// workgroup. Each wave keeps one or two steps of K/V in flight in a private
+// LDS ring while it computes the previous one. At the end the waves' (m, l, O)
+// are combined through LDS and the workgroup writes either the final fp16
+// rows (request fits one chunk) or an fp32 partial (o normalised, lse) for
+// the merge kernel. A workgroup holds at most 48 rows; a KV head with more is
+// covered by several workgroups (row tiles) that read the same keys, placed
+// on the same XCD so that the later reads are mostly served by its L2.
 #include "sv_common.h"
 
 namespace sv {
@@ -389,44 +392,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Eight 16-byte reads at addr, addr + STRIDE, ..., addr + 7*STRIDE after
 // waiting until at most VMCNT of this wave's vector-memory operations (the
 // newer half-steps) are outstanding, i.e. until the block's own DMA has
-// landed; with BARRIER the workgroup also meets, so blocks DMA-ed by the
-// partner wave have landed too.
-template <int VMCNT, bool BARRIER, int STRIDE>
+// landed.
+template <int VMCNT, int STRIDE>
 __device__ __forceinline__ void ring_read8(u32x4 (&d)[8], uint32_t addr) {
-  if constexpr (BARRIER) {
-    asm volatile(
-        "s_waitcnt vmcnt(%9)\n\t"
-        "s_barrier\n\t"
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:%10\n\t"
-        "ds_read_b128 %2, %8 offset:%11\n\t"
-        "ds_read_b128 %3, %8 offset:%12\n\t"
-        "ds_read_b128 %4, %8 offset:%13\n\t"
-        "ds_read_b128 %5, %8 offset:%14\n\t"
-        "ds_read_b128 %6, %8 offset:%15\n\t"
-        "ds_read_b128 %7, %8 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
-        : "v"(addr), "n"(VMCNT), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE), "n"(4 * STRIDE),
-          "n"(5 * STRIDE), "n"(6 * STRIDE), "n"(7 * STRIDE)
-        : "memory");
-  } else {
-    asm volatile(
-        "s_waitcnt vmcnt(%9)\n\t"
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:%10\n\t"
-        "ds_read_b128 %2, %8 offset:%11\n\t"
-        "ds_read_b128 %3, %8 offset:%12\n\t"
-        "ds_read_b128 %4, %8 offset:%13\n\t"
-        "ds_read_b128 %5, %8 offset:%14\n\t"
-        "ds_read_b128 %6, %8 offset:%15\n\t"
-        "ds_read_b128 %7, %8 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
-        : "v"(addr), "n"(VMCNT), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE), "n"(4 * STRIDE),
-          "n"(5 * STRIDE), "n"(6 * STRIDE), "n"(7 * STRIDE)
-        : "memory");
-  }
+  asm volatile(
+      "s_waitcnt vmcnt(%9)\n\t"
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+      : "v"(addr), "n"(VMCNT), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE), "n"(4 * STRIDE),
+        "n"(5 * STRIDE), "n"(6 * STRIDE), "n"(7 * STRIDE)
+      : "memory");
 }
 
 // Direct HBM -> LDS copies of 1 KB blocks [B0, B1) of one half-step; block j
@@ -839,7 +822,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     u32x4 qa[RB][8];  // the wave's Q fragments, in registers for the whole loop
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      ring_read8<63, false, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
+      ring_read8<63, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const uint32_t rows = bstart == 0 ? rows_first : step_rows(bstart);
       const int nb = min(kWave, my_steps - bstart);
@@ -918,7 +901,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     u32x4 qa[RB][8];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      ring_read8<63, false, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
+      ring_read8<63, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const uint32_t rows = bstart == 0 ? rows_first : step_rows(bstart);
       const int nb = min(kWave, my_steps - bstart);
@@ -947,7 +930,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       half4_t pb[RB];
       {
         KFrag kf;
-        ring_read8<kWait, false, 64>(kf.k, ring_lds + stage(0) + k_lane_off(lane));
+        ring_read8<kWait, 64>(kf.k, ring_lds + stage(0) + k_lane_off(lane));
         dma_k<0, 8>(step_base(min(DEPTH, nb - 1), kpool), ring + stage(0), lane);
         step_scores<RB>(kf, qa, ws, pb, lane, step_t0(0), mk, a.scale_log2);
       }
