@@ -3,11 +3,11 @@
 //
 // Stage 1 (topk_slice): one workgroup per (row, slice of 8,192 columns, or
 //   16,384 when there are few rows to spread). Each lane holds 32 (64) of the
-//   slice's values in registers; each wave finds its
-//   best k through a threshold (the k-th best lane maximum), compacts the few
-//   values that can still be in the answer, and sorts them with a 64-lane
-//   bitonic network; wave 0 sorts the 4k wave winners the same way. The
-//   logits are read once.
+//   slice's values in registers. A threshold from the k-th largest of the 64
+//   four-lane group maxima leaves the few values that can still be in the
+//   answer; they are compacted and sorted once with a 64-lane bitonic
+//   network (or, when more than 64, each wave finds its best k and wave 0
+//   merges the 4k winners). The logits are read once.
 // Stage 2 (topk_merge): one wave per row takes the best k of the slices'
 //   candidates the same way and writes them in order.
 #include <stdint.h>
@@ -98,6 +98,30 @@ __device__ __forceinline__ Cand bitonic64(Cand c, int lane) {
   c = bitonic_merge<32, 16>(c, lane);
   c = bitonic_merge<64, 32>(c, lane);
   return c;
+}
+
+// Values only, largest first (the same network).
+template <int K, int J>
+__device__ __forceinline__ float vstage(float x, int lane) {
+  const float o = __int_as_float(xor_lane<J>(__float_as_int(x), lane));
+  const bool best_first = (lane & K) == 0 || K == kWave;
+  const bool low = (lane & J) == 0;
+  return (low == best_first) ? fmaxf(x, o) : fminf(x, o);
+}
+template <int K, int J>
+__device__ __forceinline__ float vmerge(float x, int lane) {
+  x = vstage<K, J>(x, lane);
+  if constexpr (J > 1) x = vmerge<K, J / 2>(x, lane);
+  return x;
+}
+__device__ __forceinline__ float vsort64(float x, int lane) {
+  x = vmerge<2, 1>(x, lane);
+  x = vmerge<4, 2>(x, lane);
+  x = vmerge<8, 4>(x, lane);
+  x = vmerge<16, 8>(x, lane);
+  x = vmerge<32, 16>(x, lane);
+  x = vmerge<64, 32>(x, lane);
+  return x;
 }
 
 // The wave's best k (k <= 16) of the N values per lane (v, idx), in order,
@@ -223,6 +247,15 @@ __device__ __forceinline__ void slice_wave_topk(const float (&v)[NPL], int lo, i
 }
 
 // NPL values per lane: slices of NPL * 256 columns.
+//
+// The slice's answer is found with one threshold for the whole workgroup:
+// every group of 4 lanes gives its largest value, and the k-th largest t of
+// these 64 group maxima has at least k values at or above it, so the k-th
+// best value of the slice is >= t and every value of the answer is >= t.
+// The values >= t (about 18 for random data) are compacted into LDS and, when
+// they fit one per lane, sorted once by wave 0. Otherwise (many values tied
+// or clustered) each wave finds its best k with the per-wave threshold of
+// slice_wave_topk and wave 0 merges the 4k winners.
 template <bool VEC4, int NPL>
 __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __restrict__ logits, int vocab, int k,
                                                               int n_slices, float2* ws) {
@@ -249,8 +282,51 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __res
       v[u] = col < hi ? rp[col] : -INFINITY;
     }
   }
-  __shared__ Cand buf[kWavesPerGroup][kMaxTopk * NPL];
+  constexpr int kCap = kMaxTopk * NPL;  // per-wave compaction capacity
+  __shared__ Cand buf[kWavesPerGroup][kCap];
   __shared__ Cand wl[kWavesPerGroup * kMaxTopk];
+  __shared__ float s_g[kWave];
+  __shared__ int s_cnt[kWavesPerGroup];
+  // the group maxima (values past hi are -inf)
+  float m = v[0];
+#pragma unroll
+  for (int u = 1; u < NPL; ++u) m = fmaxf(m, v[u]);
+  m = fmaxf(m, __int_as_float(xor_lane<1>(__float_as_int(m), lane)));
+  m = fmaxf(m, __int_as_float(xor_lane<2>(__float_as_int(m), lane)));
+  if ((lane & 3) == 0) s_g[wave * (kWave / 4) + lane / 4] = m;
+  __syncthreads();
+  const float gs = vsort64(s_g[lane], lane);
+  const float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), k - 1));
+  // compact this wave's values >= t (the count is kept even past capacity)
+  int count = 0;
+#pragma unroll
+  for (int u = 0; u < NPL; ++u) {
+    if (__ballot(v[u] >= t)) {  // (uniform) some lane holds one here
+      const int col = slice_col(lo, tid, u);
+      const bool pred = v[u] >= t && col < hi;
+      const uint64_t mk = __ballot(pred);
+      const int pos = count + __popcll(mk & ((1ull << lane) - 1ull));
+      if (pred && pos < kCap) buf[wave][pos] = Cand{v[u], col};
+      count += __popcll(mk);
+    }
+  }
+  if (lane == 0) s_cnt[wave] = count;
+  __syncthreads();
+  const int c0 = s_cnt[0], c1 = s_cnt[1], c2 = s_cnt[2], c3 = s_cnt[3];
+  const int total = c0 + c1 + c2 + c3;  // (uniform over the workgroup)
+  if (total <= kWave) {
+    if (wave == 0) {
+      Cand c = kNone;
+      if (lane < total) {
+        const int w = lane >= c0 + c1 + c2 ? 3 : lane >= c0 + c1 ? 2 : lane >= c0 ? 1 : 0;
+        const int base = w == 0 ? 0 : w == 1 ? c0 : w == 2 ? c0 + c1 : c0 + c1 + c2;
+        c = buf[w][lane - base];
+      }
+      c = bitonic64(c, lane);
+      if (lane < k) ws[((size_t)row * n_slices + sl) * k + lane] = make_float2(c.v, __int_as_float(c.i));
+    }
+    return;
+  }
   slice_wave_topk<NPL>(v, lo, hi, tid, k, &wl[wave * k], buf[wave], lane);
   __syncthreads();
   if (wave == 0) {
