@@ -211,11 +211,12 @@ __device__ __forceinline__ float weight(const float* lp, const float* qp, float 
   return p;
 }
 
+template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void draw_kernel(SampleLaunch a) {
   const int b = blockIdx.x, tid = threadIdx.x;
-  __shared__ int s_k, s_mode, s_best, s_last;
+  __shared__ int s_k, s_mode, s_best, s_last, s_pos;
   __shared__ float s_base, s_target, s_M, s_iS;
-  __shared__ float scan[kThreads];
+  __shared__ float s_wt[kWavesPerGroup];
   const int A = a.ws_acc[b];
   const bool residual = A < a.q_len - 1;
   const size_t row = (size_t)b * a.q_len + A;
@@ -261,48 +262,70 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(SampleLaunch a) {
       s_iS = iS;
     }
   }
+  if (tid == 0) s_pos = -1;
   __syncthreads();
+  // The chosen slice: thread tid's 32 consecutive columns' weights in
+  // registers (read with 16-byte loads), their sum, the block's exclusive
+  // prefix of the sums (wave scans, then the earlier waves' totals), and the
+  // first column whose running weight passes the target.
   const float* lp = a.logits + row * a.vocab;
   const float* qp = s_mode == 1 ? a.draft_probs + ((size_t)b * (a.q_len - 1) + A) * a.vocab : nullptr;
-  const int lo = s_k * a.slice, hi = min(lo + a.slice, a.vocab);
-  const int per = a.slice / kThreads;  // consecutive columns per thread
-  const int c0 = lo + tid * per;
-  float loc = 0.f;
-  for (int i = 0; i < per; ++i)
-    if (c0 + i < hi) loc += weight(lp, qp, a.c, s_M, s_iS, c0 + i);
-  scan[tid] = loc;
-  __syncthreads();
-  // inclusive scan of the threads' sums (fixed order)
-  for (int o = 1; o < kThreads; o <<= 1) {
-    const float v = tid >= o ? scan[tid - o] : 0.f;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  const float excl = s_base + (scan[tid] - loc);
-  if (!s_last) {
-    if (excl + loc > s_target) {  // the crossing is in this thread's columns
-      float run = excl;
-      for (int i = 0; i < per; ++i) {
-        if (c0 + i >= hi) break;
-        run += weight(lp, qp, a.c, s_M, s_iS, c0 + i);
-        if (run > s_target) {
-          atomicMin(&s_best, c0 + i);
-          break;
-        }
+  const int lo = s_k * kSampleSlice, hi = min(lo + kSampleSlice, a.vocab);
+  constexpr int kPer = kSampleSlice / kThreads;  // consecutive columns per thread
+  const int c0 = lo + tid * kPer;
+  const float Mr = s_M, iS = s_iS;
+  float w[kPer];
+  if (VEC4 && c0 + kPer <= hi) {
+#pragma unroll
+    for (int j = 0; j < kPer / 4; ++j) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lp + c0 + 4 * j);
+      w[4 * j] = __builtin_amdgcn_exp2f(l4.x * a.c - Mr) * iS;
+      w[4 * j + 1] = __builtin_amdgcn_exp2f(l4.y * a.c - Mr) * iS;
+      w[4 * j + 2] = __builtin_amdgcn_exp2f(l4.z * a.c - Mr) * iS;
+      w[4 * j + 3] = __builtin_amdgcn_exp2f(l4.w * a.c - Mr) * iS;
+      if (qp) {
+        const float4 q4 = *reinterpret_cast<const float4*>(qp + c0 + 4 * j);
+        w[4 * j] = fmaxf(w[4 * j] - q4.x, 0.f);
+        w[4 * j + 1] = fmaxf(w[4 * j + 1] - q4.y, 0.f);
+        w[4 * j + 2] = fmaxf(w[4 * j + 2] - q4.z, 0.f);
+        w[4 * j + 3] = fmaxf(w[4 * j + 3] - q4.w, 0.f);
       }
     }
   } else {
-    int mine = -1;
-    for (int i = 0; i < per; ++i)
-      if (c0 + i < hi && weight(lp, qp, a.c, s_M, s_iS, c0 + i) > 0.f) mine = c0 + i;
-    if (mine >= 0) atomicMin(&s_best, -mine);  // the largest index, as a minimum of negatives
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) w[i] = c0 + i < hi ? weight(lp, qp, a.c, Mr, iS, c0 + i) : 0.f;
+  }
+  float loc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) loc += w[i];
+  const int lane = tid % kWave, wave = tid / kWave;
+  const float inc = wave_incl_scan(loc, lane);
+  if (lane == kWave - 1) s_wt[wave] = inc;
+  __syncthreads();
+  float woff = 0.f;
+  for (int v = 0; v < wave; ++v) woff += s_wt[v];
+  const float excl = s_base + woff + (inc - loc);
+  int last = -1;  // this thread's last column of positive weight
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (w[i] > 0.f) last = c0 + i;
+  if (last >= 0) atomicMax(&s_pos, last);
+  if (!s_last && excl + loc > s_target) {  // the crossing is in this thread's columns
+    float run = excl;
+    int hit = INT32_MAX;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      run += w[i];
+      if (hit == INT32_MAX && run > s_target) hit = c0 + i;
+    }
+    if (hit != INT32_MAX) atomicMin(&s_best, hit);
   }
   __syncthreads();
   if (tid == 0) {
+    // the crossing; or, when rounding put the target past the total (or past
+    // this slice's own sum), the last column of positive weight
     int tok = s_best;
-    if (s_last) tok = (tok == INT32_MAX) ? hi - 1 : -tok;
-    if (tok == INT32_MAX) tok = hi - 1;  // (cannot happen when the slice was chosen by its sum)
+    if (s_last || tok == INT32_MAX) tok = s_pos >= 0 ? s_pos : hi - 1;
     a.accept_len[b] = A;
     a.token_ids[b] = tok;
     if (a.kv_lens_out) a.kv_lens_out[b] = a.kv_lens_in[b] - a.q_len + 1 + A;
@@ -320,7 +343,10 @@ void launch_rejection_accept(const SampleLaunch& a, hipStream_t s) {
                        a.c, a.ws1);
     hipLaunchKernelGGL((walk_residual_kernel<false>), g2, dim3(kThreads), 0, s, a);
   }
-  hipLaunchKernelGGL(draw_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
+  if (a.vocab % 4 == 0)
+    hipLaunchKernelGGL((draw_kernel<true>), dim3(a.batch), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((draw_kernel<false>), dim3(a.batch), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace sv
