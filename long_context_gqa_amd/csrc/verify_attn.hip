@@ -635,6 +635,66 @@ constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
 // (more than 48 rows per KV head) they share one HBM stream, and two steps
 // each keep as many HBM bytes in flight as one step does unshared.
 
+// Dispatch order for a batch of 2..64 requests (one request per lane of the
+// wave; every wave computes the same answer): item u of the grid is the
+// u-th of all full chunks in split-major order, then the partial last
+// chunks, longest first, then nothing. Workgroups start in item order, so
+// the uneven pieces of a ragged batch go last and the largest of them
+// first (longest-processing-time order); a uniform batch keeps the
+// split-major order. A request with rows but no visible key keeps one
+// (empty) chunk, which writes its rows and flags; a request without rows (a
+// width of 0, or a bad one) has none, so item 0 reports the bad widths.
+// Returns false for an item without work.
+template <bool WIN>
+__device__ bool ordered_unit(const AttnArgs& a, int u, int lane, bool report, int* split, int* b, int* g) {
+  const int cs = a.chunk / kStep, Hkv = a.num_kv_heads;
+  int tb = 0;          // this lane's request: live 16-token steps
+  bool rows = false;   // ... and whether it has rows
+  if (lane < a.batch) {
+    int fl = 0, st = 0;
+    const int q = a.q_start ? block_rows(a.q_start, lane, a.batch, a.q_len, &st, &fl) : a.q_len;
+    if (report && (fl & 0x8) && a.flags) atomicOr(a.flags, 0x8);
+    fl = 0;
+    const int kv = clamp_kv_len(a.kv_lens[lane], a.max_kv_len, a.max_pages, a.page_size, &fl);
+    rows = q > 0;
+    if (rows) {
+      int ns, w0;
+      tb = WIN ? live_steps(kv, kv - q, a.window, a.sink, &ns, &w0) : (kv + kStep - 1) / kStep;
+    }
+  }
+  // full chunks, and the last (partial or empty) chunk if any: its length
+  const int full = tb / cs, part = tb % cs;
+  const bool has_part = part > 0 || (rows && tb == 0);
+  int i = u;
+  for (int s = 0;; ++s) {
+    const uint64_t m = __ballot(full > s);
+    if (!m) break;
+    const int n = __popcll(m) * Hkv;
+    if (i < n) {
+      const int j = i / Hkv;
+      const int rank = __popcll(m & ((1ull << lane) - 1ull));
+      *split = s;
+      *b = __builtin_ctzll(__ballot(full > s && rank == j));
+      *g = i % Hkv;
+      return true;
+    }
+    i -= n;
+  }
+  const uint64_t pm = __ballot(has_part);
+  if (i >= __popcll(pm) * Hkv) return false;
+  int rank = 0;  // among the last chunks: longer first, then lower request
+  for (int o = 0; o < a.batch; ++o) {
+    const int po = __shfl(part, o);
+    const bool ho = (pm >> o) & 1ull;
+    rank += (ho && (po > part || (po == part && o < lane))) ? 1 : 0;
+  }
+  const int bb = __builtin_ctzll(__ballot(has_part && rank == i / Hkv));
+  *b = bb;
+  *g = i % Hkv;
+  *split = __shfl(full, bb);
+  return true;
+}
+
 template <int RB, bool FP8, int DEPTH>
 struct Smem {
   static constexpr int QBYTES = RB * 8 * kWave * 16;
@@ -676,11 +736,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // Units are numbered split-major: every (KV head, request) of chunk 0,
   // then chunk 1, ... Consecutive ids (which go to consecutive XCDs) then
   // differ in head and request rather than in chunk, so ragged batches spread
-  // evenly over the XCDs, and the sparse late chunks of long requests are
-  // dispatched last.
-  const int hb = unit % (a.num_kv_heads * a.batch);
-  const int split = unit / (a.num_kv_heads * a.batch);
-  const int g = hb % a.num_kv_heads, b = hb / a.num_kv_heads;
+  // evenly over the XCDs. For 2..64 requests ordered_unit takes the full
+  // chunks in that order, then the last partial chunks, longest first.
+  int split, g, b;
+  if (a.batch > 1 && a.batch <= kWave) {
+    if (!ordered_unit<WIN>(a, unit, lane, unit == 0 && rblk == 0 && tid < kWave, &split, &b, &g)) return;
+  } else {
+    const int hb = unit % (a.num_kv_heads * a.batch);
+    split = unit / (a.num_kv_heads * a.batch);
+    g = hb % a.num_kv_heads;
+    b = hb / a.num_kv_heads;
+  }
   const int row0 = rblk * RB * 16;  // first row (of the KV head's q_len*G) of this workgroup
   int flag_bits = 0;
   // the request's block: q_len rows from packed row rstart
