@@ -2,10 +2,12 @@
 // final fp16 rows: LSE = ln sum_s exp(lse_s), out = sum_s exp(lse_s - LSE) o_s,
 // skipping empty splits (lse = -inf).
 //
-// One workgroup per (row, head). Its threads first reduce the split lse
-// values (max, then the sum of exponentials); then wave w accumulates splits
-// w, w+4, ... with each lane owning a float4 of channels and four splits'
-// loads in flight at a time; the four waves' sums are added through LDS.
+// Few items (rows x heads): one workgroup per (row, head). Its threads first
+// reduce the split lse values (max, then the sum of exponentials); then wave
+// w accumulates splits w, w+4, ... with each lane owning a float4 of channels
+// and four splits' loads in flight at a time; the four waves' sums are added
+// through LDS. Many items: one wave per (row, head), the same arithmetic
+// with wave reductions only.
 #include "sv_common.h"
 
 namespace sv {
@@ -37,12 +39,11 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
-  __shared__ float red[kWavesPerGroup];
-  __shared__ float4 acc_s[kWavesPerGroup - 1][kWave];
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  const long long item = blockIdx.x;  // (row, head)
-  const int row = (int)(item / a.num_heads);
+// The splits to merge for packed row `row`: all of them for a standalone
+// merge; for the verify entry point the chunks the attention kernel wrote
+// for the row's request (0: nothing to merge, the row was written directly
+// or belongs to no request).
+__device__ __forceinline__ int item_splits(const MergeArgs& a, int row) {
   int S = a.num_splits;
   if (a.kv_lens) {
     // merge launched by the verify entry point: a request covered by a single
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
       b = lo;
       int st = 0;
       const int n = block_rows(a.q_start, b, a.batch, a.q_len, &st, &dummy);
-      if (row < st || row >= st + n) return;
+      if (row < st || row >= st + n) return 0;
       q_b = n;
     }
     const int kv = clamp_kv_len(a.kv_lens[b], a.max_kv_len, a.max_pages, a.page_size, &dummy);
@@ -72,9 +73,20 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int total = live_steps(kv, kv - q_b, a.window, a.sink, &n_sink, &w0);
     const int cs = a.chunk / 16;
     const int nch = total > 0 ? (total + cs - 1) / cs : 1;
-    if (nch <= 1) return;
+    if (nch <= 1) return 0;
     S = min(S, nch);
   }
+  return S;
+}
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  __shared__ float red[kWavesPerGroup];
+  __shared__ float4 acc_s[kWavesPerGroup - 1][kWave];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const long long item = blockIdx.x;  // (row, head)
+  const int row = (int)(item / a.num_heads);
+  const int S = item_splits(a, row);
+  if (S <= 0) return;
   const size_t sl = (size_t)a.num_rows * a.num_heads;  // stride between splits (lse)
   const size_t so = sl * a.head_dim;                     // stride between splits (o)
   const float* lse = a.part_lse + item;
@@ -149,9 +161,79 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     a.out_lse[item] = tot > 0.f ? ref + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
 }
 
+// One wave per (row, head), for launches with many items (each with few
+// splits): wave reductions only, no workgroup barriers. Each lane owns a
+// float4 of channels and keeps four splits' loads in flight.
+__global__ __launch_bounds__(kThreads) void merge_wave_kernel(MergeArgs a) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const long long item = (long long)blockIdx.x * kWavesPerGroup + w;
+  if (item >= (long long)a.num_rows * a.num_heads) return;
+  const int row = (int)(item / a.num_heads);
+  const int S = item_splits(a, row);
+  if (S <= 0) return;
+  const size_t sl = (size_t)a.num_rows * a.num_heads;
+  const size_t so = sl * a.head_dim;
+  const float* lse = a.part_lse + item;
+  const float* po = a.part_o + item * a.head_dim;
+  float mx = -INFINITY;
+  for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, lse[s * sl]);
+  mx = wave_max(mx);
+  const float ref = (mx == -INFINITY) ? 0.f : mx;
+  float tot = 0.f;
+  for (int s = lane; s < S; s += kWave) {
+    const float l = lse[s * sl];
+    tot += (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((l - ref) * kLog2e);
+  }
+  tot = wave_sum(tot);
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const int D4 = a.head_dim / 4;
+  for (int d4 = lane; d4 < D4; d4 += kWave) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 3 < S; s += 4) {
+      float l[4];
+      float4 o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        l[u] = lse[(s + u) * sl];
+        o[u] = reinterpret_cast<const float4*>(po + (s + u) * so)[d4];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = (l[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((l[u] - ref) * kLog2e);
+        acc.x += wgt * o[u].x;
+        acc.y += wgt * o[u].y;
+        acc.z += wgt * o[u].z;
+        acc.w += wgt * o[u].w;
+      }
+    }
+    for (; s < S; ++s) {
+      const float l = lse[s * sl];
+      const float wgt = (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((l - ref) * kLog2e);
+      const float4 o = reinterpret_cast<const float4*>(po + s * so)[d4];
+      acc.x += wgt * o.x;
+      acc.y += wgt * o.y;
+      acc.z += wgt * o.z;
+      acc.w += wgt * o.w;
+    }
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 hv = {(_Float16)(acc.x * inv), (_Float16)(acc.y * inv), (_Float16)(acc.z * inv), (_Float16)(acc.w * inv)};
+    reinterpret_cast<h4*>(a.out + item * a.head_dim)[d4] = hv;
+  }
+  if (a.out_lse && lane == 0) a.out_lse[item] = tot > 0.f ? ref + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
+}
+
+// Few items (e.g. one long request: many splits each): a workgroup per item
+// spreads its splits over four waves; many items: a wave per item.
+constexpr long long kWaveMergeItems = 4096;
+
 void launch_merge(const MergeArgs& a, hipStream_t s) {
   const long long n_items = (long long)a.num_rows * a.num_heads;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, s, a);
+  if (n_items >= kWaveMergeItems)
+    hipLaunchKernelGGL(merge_wave_kernel, dim3((unsigned)((n_items + kWavesPerGroup - 1) / kWavesPerGroup)),
+                       dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace sv

@@ -1,6 +1,7 @@
 """GPU sv_verify_merge against the oracle's merge on arbitrary partials:
 many splits, empty splits (lse = -inf), fully empty rows, head_dim values
-that are not 256."""
+that are not 256, and both kernels (a workgroup per (row, head) item for
+few items, a wave per item from 4,096 items)."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +20,9 @@ def _gpu():
 
 
 @pytest.mark.parametrize("S,R,H,D", [(1, 3, 2, 256), (5, 4, 3, 100), (130, 2, 24, 256), (17, 3, 2, 1024),
-                                     (300, 1, 1, 4), (300, 2, 1, 4)])
+                                     (300, 1, 1, 4), (300, 2, 1, 4),
+                                     # 4,096 and more (row, head) items: one wave per item
+                                     (7, 200, 24, 256), (20, 171, 24, 256), (3, 4096, 1, 100), (1, 512, 24, 256)])
 def test_merge_matches_oracle(S, R, H, D):
     g = torch.Generator().manual_seed(S * 7 + D)
     po = torch.randn((S, R, H, D), generator=g) * 2
