@@ -631,9 +631,10 @@ __device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4 (&qa)
 constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
 // DEPTH steps in flight per wave in its private ring. One (64 KB per CU over
 // the four waves) saturates HBM when every workgroup streams its own keys; a
-// second step measured slower there. When two workgroups read the same keys
-// (more than 48 rows per KV head) they share one HBM stream, and two steps
-// each keep as many HBM bytes in flight as one step does unshared.
+// second step measured slower there. When several workgroups (row tiles)
+// read the same keys (more than 48 rows per KV head) they share one HBM
+// stream, and two steps each keep as many HBM bytes in flight as one step
+// does unshared.
 
 // Dispatch order for a batch of 2..64 requests (one request per lane of the
 // wave; every wave computes the same answer): item u of the grid is the

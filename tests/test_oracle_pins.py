@@ -72,6 +72,8 @@ def rand_case(rng, B, q_len, Hq, Hkv, D, P, lens, scale=1.0):
     (2, 3, 4, 2, 8, 4, [7, 12]),
     (1, 4, 6, 2, 16, 16, [21]),
     (3, 2, 2, 2, 4, 4, [2, 9, 16]),
+    (1, 40, 2, 1, 4, 4, [45]),       # an extend chunk longer than the verify blocks
+    (2, 24, 2, 2, 4, 4, [24, 30]),   # a prefill with no prefix (L = 0) and one with L = 6
 ])
 def test_attention_matches_fsum_brute_force(B, q_len, Hq, Hkv, D, P, lens):
     rng = np.random.default_rng(7)
@@ -187,12 +189,13 @@ def test_gqa_equals_mha_with_repeated_kv_heads():
     np.testing.assert_allclose(lse, lse6, rtol=0, atol=1e-14)
 
 
-def test_verify_row_equals_decode_over_prefix_plus_earlier_drafts():
+@pytest.mark.parametrize("q_len,n", [(5, 23), (33, 70)])  # a verify block, an extend chunk
+def test_verify_row_equals_decode_over_prefix_plus_earlier_drafts(q_len, n):
     rng = np.random.default_rng(4)
-    B, q_len, Hq, Hkv, D, P = 1, 5, 4, 2, 16, 4
-    q, kp, vp, table, kv = rand_case(rng, B, q_len, Hq, Hkv, D, P, [23])
+    B, Hq, Hkv, D, P = 1, 4, 2, 16, 4
+    q, kp, vp, table, kv = rand_case(rng, B, q_len, Hq, Hkv, D, P, [n])
     out, _ = oatt.verify_attention(q, kp, vp, table, kv, q_len, 0.25)
-    L = 23 - q_len
+    L = n - q_len
     for i in range(q_len):
         d, _ = oatt.decode_attention(q[i], kp, vp, table[0], L + i + 1, 0.25)
         np.testing.assert_allclose(out[i], d, rtol=0, atol=1e-15)
