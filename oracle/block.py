@@ -23,6 +23,10 @@ q_b = q_lens[b]:
 Appending writes row q_start[b] + i of the new K and V (every KV head) into
 its cache slot: pages[slot // P, h, slot % P, :] = new[row, h, :].
 
+With an FP8 cache the appended rows are quantised first (oracle.fp8,
+quantize_rows): E4M3 codes into the pages and one fp16 scale per token, KV
+head and 64-channel block into the scale pages.
+
 Readings taken (the pages name the steps but not their data layout): rows are
 packed request by request; drafts come padded as [B, max_q - 1] and the block
 ids come out packed like the rows; the cache slot is the flat index
@@ -79,3 +83,18 @@ def append_kv(pages, cache_slot, new_rows):
     for r, s in enumerate(slots):
         out[s // P, :, s % P, :] = new[r]
     return out
+
+
+def append_kv_fp8(pages, scales, cache_slot, new_rows):
+    """Copies of FP8 pages [num_pages, Hkv, P, D] (E4M3 bytes) and scales
+    [num_pages, Hkv, P, D//64] (fp16) with new_rows [rows, Hkv, D] quantised
+    (oracle.fp8.quantize_rows) and written at the given flat cache slots."""
+    from oracle.fp8 import quantize_rows
+    out, osc = _np(pages).copy(), _np(scales).copy()
+    slots = _np(cache_slot).astype(np.int64)
+    codes, sc = quantize_rows(_np(new_rows))
+    P = out.shape[2]
+    for r, s in enumerate(slots):
+        out[s // P, :, s % P, :] = codes[r]
+        osc[s // P, :, s % P, :] = sc[r]
+    return out, osc
