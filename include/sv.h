@@ -285,7 +285,7 @@ sv_status sv_prepare_block(const int32_t* seq_lens, const int32_t* q_lens, const
  *   q_start       [batch+1] int32 (e.g. from sv_prepare_block)
  *   max_rows      host bound on q_start[batch]: sizes the grid
  *   k_pages, v_pages  [num_pages, num_kv_heads, page_size, head_dim], written
- *   kv_dtype      SV_KV_FP16 only (FP8 pages: SV_ERR_UNSUPPORTED)
+ *   kv_dtype      SV_KV_FP16 only (FP8 pages: SV_ERR_UNSUPPORTED; use sv_append_kv_fp8)
  * Rows that share a slot race; prepare_block never gives two rows one slot
  * when the page table maps distinct positions to distinct slots.
  */
@@ -293,6 +293,30 @@ sv_status sv_append_kv(const void* new_k, const void* new_v, const int32_t* cach
                        int32_t batch, int32_t max_rows, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                        int32_t num_pages, sv_kv_dtype kv_dtype, void* k_pages, void* v_pages,
                        int32_t* status_flags, void* stream);
+
+/*
+ * The same append into an FP8 cache (the E4M3 pages with one fp16 scale per
+ * token, KV head and 64-channel block of the page "Qwen3.8-27B-FP8",
+ * sections "Implemented execution path" and "KV cache dtype and the
+ * 262,144-token boundary"): each new row is quantised per 64-channel block,
+ *     scale = fp16(amax / 448)   (amax = largest |x| of the block; 1.0 where
+ *                                 the fp16 value would be 0)
+ *     code  = E4M3 of clamp(x / scale, -448, 448), nearest value, ties to
+ *             the even code, the sign kept (-0 gives 0x80)
+ * with both divisions in fp32 rounded to nearest, and written with its scales:
+ *     k_pages[slot / P, h, slot % P, :]        = codes of new_k[r, h, :]
+ *     k_scales[slot / P, h, slot % P, 0..D/64) = their scales   (same for V)
+ *
+ *   new_k, new_v  [rows, num_kv_heads, head_dim] fp16, 8-byte aligned
+ *   head_dim      a multiple of 64 (the verify attention reads 256)
+ *   k_pages, v_pages    [num_pages, num_kv_heads, page_size, head_dim] uint8, 4-byte aligned
+ *   k_scales, v_scales  [num_pages, num_kv_heads, page_size, head_dim/64] fp16
+ *   other arguments, the skipped and flagged slots and the races as in sv_append_kv.
+ */
+sv_status sv_append_kv_fp8(const void* new_k, const void* new_v, const int32_t* cache_slot, const int32_t* q_start,
+                           int32_t batch, int32_t max_rows, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t num_pages, void* k_pages, void* v_pages, void* k_scales,
+                           void* v_scales, int32_t* status_flags, void* stream);
 
 /* Bytes of workspace sv_rejection_accept needs. */
 size_t sv_rejection_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vocab);

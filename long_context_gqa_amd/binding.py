@@ -24,7 +24,8 @@ SV_FLAG_BAD_BLOCK_WIDTH = 8
 EXPORTED = (
     "sv_verify_workspace_bytes", "sv_verify_plan", "sv_verify_attention", "sv_verify_merge",
     "sv_greedy_accept_workspace_bytes", "sv_greedy_accept", "sv_verify_attention_ragged",
-    "sv_greedy_accept_ragged", "sv_prepare_block", "sv_append_kv", "sv_rejection_accept_workspace_bytes",
+    "sv_greedy_accept_ragged", "sv_prepare_block", "sv_append_kv", "sv_append_kv_fp8",
+    "sv_rejection_accept_workspace_bytes",
     "sv_rejection_accept", "sv_topk_candidates_workspace_bytes", "sv_topk_candidates", "sv_status_string",
     "sv_last_error", "sv_version",
 )
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.sv_prepare_block.restype = ctypes.c_int
         L.sv_append_kv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp]
         L.sv_append_kv.restype = ctypes.c_int
+        L.sv_append_kv_fp8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.sv_append_kv_fp8.restype = ctypes.c_int
         L.sv_rejection_accept_workspace_bytes.argtypes = [i32, i32, i32]
         L.sv_rejection_accept_workspace_bytes.restype = sz
         L.sv_rejection_accept.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -211,6 +214,16 @@ def sv_append_kv(new_k, new_v, cache_slot, q_start, batch, max_rows, k_pages, v_
     _check(lib().sv_append_kv(_ptr(new_k), _ptr(new_v), _ptr(cache_slot), _ptr(q_start), batch, max_rows, Hkv, D, P,
                               num_pages, SV_KV_FP16 if k_pages.dtype == torch.float16 else SV_KV_FP8_E4M3,
                               _ptr(k_pages), _ptr(v_pages), _ptr(status_flags), _stream(stream)))
+
+
+def sv_append_kv_fp8(new_k, new_v, cache_slot, q_start, batch, max_rows, k_pages, v_pages, k_scales, v_scales,
+                     status_flags=None, stream=None):
+    """Quantise new fp16 K/V rows per 64-channel block into E4M3 pages (uint8)
+    and their fp16 scale pages at the rows' cache slots."""
+    num_pages, Hkv, P, D = k_pages.shape
+    _check(lib().sv_append_kv_fp8(_ptr(new_k), _ptr(new_v), _ptr(cache_slot), _ptr(q_start), batch, max_rows, Hkv, D,
+                                  P, num_pages, _ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales),
+                                  _ptr(status_flags), _stream(stream)))
 
 
 def sv_rejection_accept_workspace_bytes(batch: int, q_len: int, vocab: int) -> int:

@@ -102,8 +102,94 @@ __global__ __launch_bounds__(kThreads) void append_kv_kernel(AppendArgs a) {
   *reinterpret_cast<uint4*>(a.v_pages + dst) = vv;
 }
 
+// E4M3 byte of y (|y| <= 448): the nearest finite value, ties to the even
+// code, the sign of y kept. Normal range (|y| >= 2^-6): the fp32 mantissa
+// rounded to 3 bits, to nearest even; below it, multiples of 2^-9 (2^-6 itself
+// is code 0x08).
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float ay = fabsf(y);
+  uint32_t code;
+  if (ay >= 0.015625f) {
+    const uint32_t ab = __float_as_uint(ay);
+    int e = (int)(ab >> 23) - 127;  // -6 .. 8
+    uint32_t q = (ab >> 20) & 7u;
+    const uint32_t rem = ab & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    if (q == 8u) {
+      q = 0u;
+      ++e;
+    }
+    code = ((uint32_t)(e + 7) << 3) | q;
+  } else {
+    code = (uint32_t)rintf(ay * 512.f);  // exact scaling; round to nearest even
+  }
+  return sign | code;
+}
+
+// One wave per (row, KV head): lane l quantises channels 4l .. 4l+3 of each
+// 256-channel group; the 16 lanes of a 64-channel block share its largest
+// |x|. scale = fp16(amax / 448) (1.0 where that is 0), code = E4M3 of
+// clamp(x / scale, +-448); both divisions rounded to nearest.
+__global__ __launch_bounds__(kThreads) void append_kv_fp8_kernel(AppendFp8Args a) {
+  const int lane = threadIdx.x % kWave;
+  const long long item = (long long)blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
+  const int row = (int)(item / a.num_kv_heads), h = (int)(item % a.num_kv_heads);
+  if (row >= a.max_rows) return;
+  if (row < a.q_start[0] || row >= a.q_start[a.batch]) return;
+  const int slot = a.cache_slot[row];
+  if (slot < 0) return;
+  if ((long long)slot >= (long long)a.num_pages * a.page_size) {
+    if (a.flags && lane == 0) atomicOr(a.flags, 0x4);
+    return;
+  }
+  const int page = slot / a.page_size, s = slot % a.page_size;
+  const size_t src = ((size_t)row * a.num_kv_heads + h) * a.head_dim;
+  const size_t dst = (((size_t)page * a.num_kv_heads + h) * a.page_size + s) * a.head_dim;
+  const int nb = a.head_dim / 64;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const _Float16* in = (kv ? a.new_v : a.new_k) + src;
+    uint8_t* out = (kv ? a.v_pages : a.k_pages) + dst;
+    _Float16* sc_out = (kv ? a.v_scales : a.k_scales) + dst / 64;
+    for (int c0 = 4 * lane; c0 - 4 * lane < a.head_dim; c0 += 4 * kWave) {
+      const bool on = c0 < a.head_dim;  // (uniform trip count: every lane shuffles)
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (on) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 v = *reinterpret_cast<const h4*>(in + c0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = (float)v[k];
+      }
+      float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      _Float16 sc = (_Float16)__fdiv_rn(m, 448.f);
+      if (sc == (_Float16)0.f) sc = (_Float16)1.f;
+      if (on) {
+        const float fs = (float)sc;
+        uint32_t packed = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float y = fminf(fmaxf(__fdiv_rn(x[k], fs), -448.f), 448.f);
+          packed |= e4m3_rne(y) << (8 * k);
+        }
+        *reinterpret_cast<uint32_t*>(out + c0) = packed;
+        if ((lane & 15) == 0 && c0 / 64 < nb) sc_out[c0 / 64] = sc;
+      }
+    }
+  }
+}
+
 void launch_prepare_block(const PrepareArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prepare_block_kernel, dim3(1), dim3(kThreads), 0, s, a);
+}
+
+void launch_append_kv_fp8(const AppendFp8Args& a, hipStream_t s) {
+  const long long items = (long long)a.max_rows * a.num_kv_heads;  // one wave each
+  const long long groups = (items + kWavesPerGroup - 1) / kWavesPerGroup;
+  hipLaunchKernelGGL(append_kv_fp8_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, a);
 }
 
 void launch_append_kv(const AppendArgs& a, hipStream_t s) {

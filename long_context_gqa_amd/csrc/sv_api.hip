@@ -461,7 +461,8 @@ sv_status sv_append_kv(const void* new_k, const void* new_v, const int32_t* cach
                        int32_t* status_flags, void* stream) {
   if (batch < 1 || max_rows < 1 || num_kv_heads < 1)
     return fail(SV_ERR_INVALID_ARGUMENT, "batch, max_rows and num_kv_heads must be >= 1");
-  if (kv_dtype != SV_KV_FP16) return fail(SV_ERR_UNSUPPORTED, "sv_append_kv writes fp16 pages only");
+  if (kv_dtype != SV_KV_FP16)
+    return fail(SV_ERR_UNSUPPORTED, "sv_append_kv writes fp16 pages only (FP8 pages: sv_append_kv_fp8)");
   if (head_dim < 8 || head_dim % 8 != 0 || head_dim > 4096)
     return fail(SV_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in 8..4096 (got %d)", head_dim);
   if (page_size < 1 || num_pages < 1)
@@ -491,6 +492,47 @@ sv_status sv_append_kv(const void* new_k, const void* new_v, const int32_t* cach
   a.num_pages = num_pages;
   sv::launch_append_kv(a, static_cast<hipStream_t>(stream));
   return check_launch("append_kv");
+}
+
+sv_status sv_append_kv_fp8(const void* new_k, const void* new_v, const int32_t* cache_slot, const int32_t* q_start,
+                           int32_t batch, int32_t max_rows, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t num_pages, void* k_pages, void* v_pages, void* k_scales,
+                           void* v_scales, int32_t* status_flags, void* stream) {
+  if (batch < 1 || max_rows < 1 || num_kv_heads < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "batch, max_rows and num_kv_heads must be >= 1");
+  if (head_dim < 64 || head_dim % 64 != 0 || head_dim > 4096)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be a multiple of 64 in 64..4096 (got %d)", head_dim);
+  if (page_size < 1 || num_pages < 1)
+    return fail(SV_ERR_INVALID_ARGUMENT, "page_size and num_pages must be >= 1");
+  if ((long long)num_pages * page_size > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "num_pages * page_size must fit in int32 (flat cache slots)");
+  if ((long long)max_rows * num_kv_heads > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "too many rows");
+  if (!new_k || !new_v || !cache_slot || !q_start || !k_pages || !v_pages || !k_scales || !v_scales)
+    return fail(SV_ERR_INVALID_ARGUMENT,
+                "new_k, new_v, cache_slot, q_start, k_pages, v_pages, k_scales and v_scales must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 8 ||
+      (reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) % 4 ||
+      (reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) % 2)
+    return fail(SV_ERR_INVALID_ARGUMENT, "new_k/new_v must be 8-byte, pages 4-byte and scales 2-byte aligned");
+  sv::AppendFp8Args a;
+  a.new_k = static_cast<const _Float16*>(new_k);
+  a.new_v = static_cast<const _Float16*>(new_v);
+  a.cache_slot = cache_slot;
+  a.q_start = q_start;
+  a.k_pages = static_cast<uint8_t*>(k_pages);
+  a.v_pages = static_cast<uint8_t*>(v_pages);
+  a.k_scales = static_cast<_Float16*>(k_scales);
+  a.v_scales = static_cast<_Float16*>(v_scales);
+  a.flags = status_flags;
+  a.batch = batch;
+  a.max_rows = max_rows;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  sv::launch_append_kv_fp8(a, static_cast<hipStream_t>(stream));
+  return check_launch("append_kv_fp8");
 }
 
 size_t sv_rejection_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vocab) {

@@ -33,7 +33,22 @@ struct AppendArgs {
   int32_t batch, max_rows, num_kv_heads, head_dim, page_size, num_pages;
 };
 
+// Appending into an FP8 cache: the rows are quantised per 64-channel block.
+struct AppendFp8Args {
+  const _Float16* new_k;  // [rows, Hkv, D]
+  const _Float16* new_v;
+  const int32_t* cache_slot;
+  const int32_t* q_start;  // [batch+1]
+  uint8_t* k_pages;        // [num_pages, Hkv, P, D] E4M3 codes
+  uint8_t* v_pages;
+  _Float16* k_scales;      // [num_pages, Hkv, P, D/64]
+  _Float16* v_scales;
+  int32_t* flags;
+  int32_t batch, max_rows, num_kv_heads, head_dim, page_size, num_pages;
+};
+
 void launch_prepare_block(const PrepareArgs& a, hipStream_t s);
 void launch_append_kv(const AppendArgs& a, hipStream_t s);
+void launch_append_kv_fp8(const AppendFp8Args& a, hipStream_t s);
 
 }  // namespace sv

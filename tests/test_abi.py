@@ -172,6 +172,16 @@ def test_block_entry_points_reject_bad_arguments_without_launch():
     assert st == B.SV_ERR_INVALID_ARGUMENT  # misaligned
     st = lib.sv_append_kv(None, fake, fake, fake, 2, 16, 4, 256, 16, 100, B.SV_KV_FP16, fake, fake, None, None)
     assert st == B.SV_ERR_INVALID_ARGUMENT
+    # append_kv_fp8: head_dim a multiple of 64, scale pages required, alignment
+    st = lib.sv_append_kv_fp8(fake, fake, fake, fake, 2, 16, 4, 96, 16, 100, fake, fake, fake, fake, None, None)
+    assert st == B.SV_ERR_UNSUPPORTED
+    st = lib.sv_append_kv_fp8(fake, fake, fake, fake, 2, 16, 4, 256, 16, 100, fake, fake, None, fake, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT and b"k_scales" in lib.sv_last_error()
+    st = lib.sv_append_kv_fp8(fake + 4, fake, fake, fake, 2, 16, 4, 256, 16, 100, fake, fake, fake, fake, None,
+                              None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT  # new_k not 8-byte aligned
+    st = lib.sv_append_kv_fp8(fake, fake, fake, fake, 0, 16, 4, 256, 16, 100, fake, fake, fake, fake, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT
 
 
 def test_rejection_accept_rejects_bad_arguments_without_launch():

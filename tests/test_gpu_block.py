@@ -292,6 +292,102 @@ def test_whole_round_prepare_append_verify_accept():
     assert np.array_equal(acc[3].cpu().numpy(), rn)
 
 
+def test_append_kv_fp8_matches_oracle_bitwise():
+    # quantised rows (E4M3 codes and fp16 scales) in their slots, bit-exact:
+    # scales spanning fp16, zero and negative-zero blocks, exact ties of the
+    # rounding, values at +-65504, subnormal codes; slot -1 skipped, a slot
+    # past the pool flagged
+    rng = np.random.default_rng(9)
+    Bn, qmax, P, Hkv, D = 5, 16, 16, 4, 256
+    widths = np.array([16, 3, 0, 9, 1])
+    L = rng.integers(0, 300, Bn)
+    npg = (L + widths + P - 1) // P
+    num_pages = int(npg.sum()) + 2
+    table = np.full((Bn, int(npg.max())), -1, dtype=np.int32)
+    perm, off = rng.permutation(num_pages), 0
+    for b in range(Bn):
+        table[b, :npg[b]] = perm[off:off + npg[b]]
+        off += npg[b]
+    r = oblk.prepare_block(L, widths, table, P)
+    n = int(r["q_start"][-1])
+    g = torch.Generator().manual_seed(4)
+    mag = torch.tensor([1e-4, 1.0, 37.0, 2000.0])[torch.randint(0, 4, (Bn * qmax, Hkv, D // 64), generator=g)]
+    nk = (torch.randn((Bn * qmax, Hkv, D), generator=g) * mag.repeat_interleave(64, -1)).half()
+    nv = (torch.randn((Bn * qmax, Hkv, D), generator=g) * mag.repeat_interleave(64, -1)).half()
+    nk[0, 0, :64] = 0.0
+    nk[1, 1, 64:128] = -0.0
+    nk[2, 2, :64] = torch.tensor([448.0, -448.0, 65504.0, -65504.0] * 16).half()
+    # x / scale exactly halfway between two codes (scale 1: amax 448): 12.5 between 12 and 13,
+    # 2.5 * 2^-9 between the subnormals 2 * 2^-9 and 3 * 2^-9 (both to the even code)
+    nv[3, 0, :64] = torch.tensor([448.0, 12.5, 2.5 * 0.001953125, 3.0 * 0.001953125] * 16).half()
+    kp = torch.randint(0, 256, (num_pages, Hkv, P, D), generator=g, dtype=torch.uint8)
+    vp = torch.randint(0, 256, (num_pages, Hkv, P, D), generator=g, dtype=torch.uint8)
+    ks = torch.rand((num_pages, Hkv, P, D // 64), generator=g).half()
+    vs = torch.rand((num_pages, Hkv, P, D // 64), generator=g).half()
+    slots = torch.full((Bn * qmax,), -1, dtype=torch.int32)
+    slots[:n] = torch.tensor(r["cache_slot"], dtype=torch.int32)
+    slots[n - 1] = -1  # skipped
+    kd, vd, ksd, vsd = kp.cuda(), vp.cuda(), ks.cuda(), vs.cuda()
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qs = torch.tensor(r["q_start"], dtype=torch.int32).cuda()
+    B.sv_append_kv_fp8(nk.cuda(), nv.cuda(), slots.cuda(), qs, Bn, Bn * qmax, kd, vd, ksd, vsd, flags)
+    torch.cuda.synchronize()
+    assert flags.item() == 0
+    used = r["cache_slot"][: n - 1]
+    ek, eks = oblk.append_kv_fp8(kp.numpy(), ks.numpy(), used, nk[: n - 1].numpy())
+    ev, evs = oblk.append_kv_fp8(vp.numpy(), vs.numpy(), used, nv[: n - 1].numpy())
+    assert np.array_equal(kd.cpu().numpy(), ek) and np.array_equal(vd.cpu().numpy(), ev)
+    assert np.array_equal(ksd.cpu().numpy().view(np.uint16), eks.view(np.uint16))
+    assert np.array_equal(vsd.cpu().numpy().view(np.uint16), evs.view(np.uint16))
+    # a slot past the pool: skipped and flagged
+    slots2 = slots.clone()
+    slots2[0] = num_pages * P + 5
+    flags.zero_()
+    B.sv_append_kv_fp8(nk.cuda(), nv.cuda(), slots2.cuda(), qs, Bn, Bn * qmax, kd, vd, ksd, vsd, flags)
+    torch.cuda.synchronize()
+    assert flags.item() == B.SV_FLAG_PAGE_ID_OUT_OF_RANGE
+
+
+def test_whole_round_with_an_fp8_cache():
+    # prepare -> FP8 append (quantised) -> FP8 ragged verify -> accept, against
+    # the oracle's steps in the same order
+    widths, prefixes, P, qmax, Hq, Hkv, D = [5, 16, 2, 8], [700, 30, 1500, 255], 16, 16, 24, 4, 256
+    Bn = len(widths)
+    x, _, _, _, _ = ragged_case([qmax] * Bn, prefixes, P, kv_dtype="fp8_e4m3", seed=41)
+    table = x.page_table
+    rng = np.random.default_rng(5)
+    last = rng.integers(0, 1000, Bn).astype(np.int32)
+    drafts = rng.integers(0, 1000, (Bn, qmax - 1)).astype(np.int32)
+    prep = B.PrepareCall(torch.tensor(prefixes, dtype=torch.int32).cuda(), torch.tensor(widths, dtype=torch.int32).cuda(),
+                         table.cuda(), qmax, P, x.num_pages, torch.tensor(last).cuda(), torch.tensor(drafts).cuda()).run()
+    g = torch.Generator(device="cuda").manual_seed(13)
+    n = sum(widths)
+    nk = torch.randn((Bn * qmax, Hkv, D), generator=g, device="cuda").half()
+    nv = torch.randn((Bn * qmax, Hkv, D), generator=g, device="cuda").half()
+    q = torch.randn((n, Hq, D), generator=g, device="cuda").half()
+    kp0, vp0, ks0, vs0 = x.k_pages.cpu(), x.v_pages.cpu(), x.k_scales.cpu(), x.v_scales.cpu()
+    B.sv_append_kv_fp8(nk, nv, prep.cache_slot, prep.q_start, Bn, Bn * qmax, x.k_pages, x.v_pages, x.k_scales,
+                       x.v_scales, prep.flags)
+    c = B.RaggedVerifyCall(q, prep.q_start, x.k_pages, x.v_pages, table.cuda(), prep.kv_lens_out, qmax,
+                           max(prefixes) + qmax, x.k_scales, x.v_scales, x.sm_scale)
+    out, lse = c.run()
+    logits = torch.randn((n, 5000), generator=g, device="cuda")
+    acc = B.RaggedAcceptCall(logits, prep.block_ids, prep.q_start, Bn, qmax, prep.kv_lens_out).run()
+    torch.cuda.synchronize()
+    assert prep.flags.item() == 0 and c.flags.item() == 0
+    r = oblk.prepare_block(prefixes, widths, table, P, last, drafts)
+    kp, ks = oblk.append_kv_fp8(kp0.numpy(), ks0.numpy(), r["cache_slot"], nk[:n].cpu().numpy())
+    vp, vs = oblk.append_kv_fp8(vp0.numpy(), vs0.numpy(), r["cache_slot"], nv[:n].cpu().numpy())
+    assert np.array_equal(x.k_pages.cpu().numpy(), kp) and np.array_equal(x.v_scales.cpu().numpy().view(np.uint16),
+                                                                           vs.view(np.uint16))
+    ref, ref_lse = oatt.verify_attention_ragged(q.cpu(), kp, vp, table, r["kv_lens_out"], np.array(widths),
+                                                r["q_start"], x.sm_scale, ks, vs)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), ref, ref_lse, what="FP8 round attention")
+    ra, rb, ram, rn = oacc.greedy_accept_ragged(logits.cpu().numpy(), r["block_ids"], np.array(widths),
+                                                r["q_start"], r["kv_lens_out"])
+    assert np.array_equal(acc[0].cpu().numpy(), ra) and np.array_equal(acc[3].cpu().numpy(), rn)
+
+
 @pytest.mark.parametrize("variant", ["literal", "unit"])
 def test_ragged_full_size_8k_131k_sampled(variant):
     # the ragged 32-request workload (64-token pages, shared pool) with seeded
