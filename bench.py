@@ -389,9 +389,10 @@ def main():
 
 def ragged_round(x, wl, acc_in, page_table, stream, timed, n):
     """One verify round with a seeded width per request (2..q_len), on the
-    workload's cache: prepare_block, append_kv (rewriting the block rows with
-    the values already there, so the pool is unchanged), ragged verify
-    attention and ragged greedy accept, each timed alone."""
+    workload's cache: prepare_block, the K/V append (rewriting the block rows
+    with the values already there; an FP8 cache gets them dequantised and
+    quantised again), ragged verify attention and ragged greedy accept, each
+    timed alone."""
     import numpy as np
     import torch
 
@@ -414,9 +415,9 @@ def ragged_round(x, wl, acc_in, page_table, stream, timed, n):
     res = {"widths": widths, "rows": rows, "batch": wl.batch, "max_width": q}
     res["prepare_us"] = round(float(np.median(timed(lambda: prep.run(stream), n))), 2)
 
+    P = wl.page_size
+    sl = prep.cache_slot[:rows].long()
     if wl.kv_dtype == "fp16":
-        P = wl.page_size
-        sl = prep.cache_slot[:rows].long()
         nk = x.k_pages[sl // P, :, sl % P].contiguous()
         nv = x.v_pages[sl // P, :, sl % P].contiguous()
         ab = 2 * 2 * nk.numel() * 2 + rows * 4  # K and V rows read and written, slots read
@@ -424,9 +425,21 @@ def ragged_round(x, wl, acc_in, page_table, stream, timed, n):
         def app():
             B.sv_append_kv(nk, nv, prep.cache_slot, prep.q_start, wl.batch, wl.batch * q, x.k_pages, x.v_pages,
                            prep.flags, stream)
-        app()
-        us = float(np.median(timed(app, n)))
-        res.update(append_us=round(us, 2), append_GBps=round(ab / (us * 1e-6) / 1e9, 1), append_bytes=ab)
+    else:
+        # the rows' dequantised values, quantised again into their slots
+        def deq(pages, scales):
+            codes = pages[sl // P, :, sl % P].contiguous().view(torch.float8_e4m3fn).to(torch.float32)
+            return (codes * scales[sl // P, :, sl % P].float().repeat_interleave(64, -1)).to(torch.float16)
+        nk, nv = deq(x.k_pages, x.k_scales), deq(x.v_pages, x.v_scales)
+        # fp16 rows read; E4M3 codes and fp16 scales written; slots read
+        ab = 2 * (nk.numel() * 2 + nk.numel() + nk.numel() // 64 * 2) + rows * 4
+
+        def app():
+            B.sv_append_kv_fp8(nk, nv, prep.cache_slot, prep.q_start, wl.batch, wl.batch * q, x.k_pages, x.v_pages,
+                               x.k_scales, x.v_scales, prep.flags, stream)
+    app()
+    us = float(np.median(timed(app, n)))
+    res.update(append_us=round(us, 2), append_GBps=round(ab / (us * 1e-6) / 1e9, 1), append_bytes=ab)
 
     qp = W.pack_rows(x.q, q, widths)
     rc = B.RaggedVerifyCall(qp, prep.q_start, x.k_pages, x.v_pages, page_table, prep.kv_lens_out, q, x.max_kv_len,
