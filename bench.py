@@ -162,8 +162,11 @@ def main():
     if call.splits > 1:
         S, R, Hq, D = call.splits, x.q.shape[0], x.q.shape[1], x.q.shape[2]
         po_bytes = S * R * Hq * D * 4
-        po = call.workspace[:po_bytes].view(torch.float32).view(S, R, Hq, D)
-        off = (po_bytes + 255) // 256 * 256
+        # the workspace: a block of work counters, then the partials (O, then lse)
+        a256 = lambda n: (n + 255) // 256 * 256
+        base = call.workspace.numel() - a256(po_bytes) - a256(S * R * Hq * 4)
+        po = call.workspace[base:base + po_bytes].view(torch.float32).view(S, R, Hq, D)
+        off = base + a256(po_bytes)
         pl = call.workspace[off:off + S * R * Hq * 4].view(torch.float32).view(S, R, Hq)
         mout = torch.empty_like(x.q)
         merge_us = timed(lambda: B.sv_verify_merge(po, pl, mout, None, stream), n_part)

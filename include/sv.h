@@ -50,6 +50,9 @@ typedef enum { SV_KV_FP16 = 0, SV_KV_FP8_E4M3 = 1 } sv_kv_dtype;
                                            (sv_prepare_block, sv_append_kv: the row's slot is -1 / skipped) */
 #define SV_FLAG_BAD_BLOCK_WIDTH 0x8 /* a width outside 0..max, or packed rows outside 0..batch*max;
                                        that request is treated as having no block */
+#define SV_FLAG_WORKSPACE_NOT_ZERO 0x10 /* the work counters in the first 32 KB of the verify
+                                           workspace were not zero at the call: the result is wrong
+                                           (they are zero again afterwards) */
 
 /*
  * Shape and layout of one verify call (host struct).
@@ -94,7 +97,12 @@ typedef struct {
 
 /*
  * Bytes of workspace sv_verify_attention needs for these parameters (0 when
- * one key chunk covers max_kv_len). Depends only on the host fields.
+ * one key chunk covers max_kv_len). Depends only on the host fields. Its
+ * first 32 KB hold work counters and must be zero before the workspace's
+ * first use, e.g. filled with zeros once when it is allocated: every verify
+ * call leaves them zero again, so a workspace serves any number of verify
+ * calls (also of other shapes), one at a time, but should not be shared with
+ * other entry points' scratch. The partials follow.
  */
 size_t sv_verify_workspace_bytes(const sv_verify_params* p);
 
@@ -128,11 +136,17 @@ sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t
  *   out_lse     NULL or [batch*q_len, Hq] fp32: natural-log sum of
  *               exp(sm_scale * q.k) over the row's visible keys
  *   workspace   device buffer of sv_verify_workspace_bytes(p) bytes, 256-byte
- *               aligned; contents need no initialisation
+ *               aligned; its first 32 KB zero (see sv_verify_workspace_bytes)
  *   status_flags NULL or one int32 word (see SV_FLAG_*)
  *
  * Arithmetic: fp16 (or exactly dequantised E4M3) inputs, fp32 accumulation;
  * the result does not depend on the number of splits beyond rounding.
+ * Repeated calls give the same bits, except for one request with fp16 keys,
+ * full attention, q_len*Hq/Hkv <= 48, a split count that is a multiple of 8
+ * and max_kv_len >= 4096 * splits (at least 64 key steps of 16 per wave;
+ * e.g. 256K tokens at the automatic 64 splits): there the waves of each KV
+ * head claim 64-key grains at run time, so the order of the softmax
+ * updates, and with it the rounding, varies between calls.
  */
 sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const void* k_pages,
                               const void* v_pages, const void* k_scales, const void* v_scales,

@@ -275,7 +275,8 @@ class VerifyCall:
         self.out = torch.empty_like(q)
         self.out_lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=dev) if with_lse else None
         nbytes = sv_verify_workspace_bytes(self.params)
-        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        # zero-filled once: its first 32 KB are work counters every call leaves at zero
+        self.workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
         self.splits, self.chunk = sv_verify_plan(self.params)
 
@@ -343,7 +344,8 @@ class RaggedVerifyCall:
         self.out = torch.empty_like(q)
         self.out_lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=dev) if with_lse else None
         nbytes = sv_verify_workspace_bytes(self.params)
-        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        # zero-filled once: its first 32 KB are work counters every call leaves at zero
+        self.workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
         self.splits, self.chunk = sv_verify_plan(self.params)
 

@@ -45,6 +45,7 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 // or belongs to no request).
 __device__ __forceinline__ int item_splits(const MergeArgs& a, int row) {
   int S = a.num_splits;
+  if (a.counters) return S;  // claimed work: every workgroup wrote its slot
   if (a.kv_lens) {
     // merge launched by the verify entry point: a request covered by a single
     // chunk was written directly, and chunks past its length hold nothing
@@ -79,7 +80,28 @@ __device__ __forceinline__ int item_splits(const MergeArgs& a, int row) {
   return S;
 }
 
+// Claimed work: each grain counter must have ended at the number of grains
+// it deals plus the number of waves that claim from it (each fails once);
+// anything else means it did not start at zero (bit 0x10). Either way it is
+// left at zero for the next call. Runs once, in block 0, after the attention
+// kernel has finished.
+__device__ __forceinline__ void settle_counters(const MergeArgs& a) {
+  if (!a.counters || blockIdx.x != 0 || (int)threadIdx.x >= a.num_kv_heads * kClaimCounters) return;
+  int dummy = 0;
+  const int kv = clamp_kv_len(a.kv_lens[0], a.max_kv_len, a.max_pages, a.page_size, &dummy);
+  int f, pool0, n_grains;
+  claim_layout(kv > 0 ? (kv + 15) / 16 : 0, a.num_splits, &f, &pool0, &n_grains);
+  // counter c of C deals its grains to S / 2 / C * 8 waves, each of which
+  // fails once; counters past C are not used
+  const int C = claim_counters(a.num_splits), c = (int)threadIdx.x % kClaimCounters;
+  const int want = c < C ? counter_grains(n_grains, c, C) + a.num_splits / 2 / C * 8 : 0;
+  int32_t* const ctr = a.counters + threadIdx.x * kCounterStride;
+  if (*ctr != want && a.flags) atomicOr(a.flags, 0x10);
+  *ctr = 0;
+}
+
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  settle_counters(a);
   __shared__ float red[kWavesPerGroup];
   __shared__ float4 acc_s[kWavesPerGroup - 1][kWave];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -165,6 +187,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 // splits): wave reductions only, no workgroup barriers. Each lane owns a
 // float4 of channels and keeps four splits' loads in flight.
 __global__ __launch_bounds__(kThreads) void merge_wave_kernel(MergeArgs a) {
+  settle_counters(a);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const long long item = (long long)blockIdx.x * kWavesPerGroup + w;
   if (item >= (long long)a.num_rows * a.num_heads) return;

@@ -58,8 +58,13 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Plan {
   int rb, row_blocks;  // row blocks of 16 per workgroup; workgroups per (chunk, KV head, request)
   int splits, chunk;   // key chunks and their length in tokens
+  bool claim;          // one request: its KV heads' keys are claimed in grains (splits = slots per head)
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
+
+// The first 256 bytes of a split workspace hold the claimed-work counters
+// (one int32 per KV head); the partials follow.
+constexpr size_t kCounterBytes = sv::kCounterSlots * sv::kCounterStride * 4;
 
 constexpr int kMinChunk = 128;         // tokens; below this the partial traffic dominates
 constexpr int kBatchChunkCap = 8192;   // tokens; largest automatic chunk for a batch of requests
@@ -157,16 +162,30 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   S = (maxkv + chunk - 1) / chunk;
   if (S * p->num_kv_heads * p->batch * 2 * rgs > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "too many workgroups (%lld splits)", S);
+  // One long request with fp16 keys, full attention and one row tile: its
+  // workgroups (S a multiple of 8, so every KV head has workgroups on all 8
+  // XCDs) claim the keys in grains, which evens out XCDs that stream at
+  // different rates. Only where every wave has about 64 steps or more.
+  pl->claim = false;
+  if (p->batch == 1 && p->window == 0 && p->kv_dtype == SV_KV_FP16 && pl->row_blocks == 1 &&
+      p->num_kv_heads * sv::kClaimCounters <= sv::kCounterSlots) {
+    const long long S8 = p->num_splits > 0 ? S : (S + 7) / 8 * 8;
+    if (S8 >= 8 && S8 % 8 == 0 && (maxkv + 15) / 16 >= 64LL * sv::kWavesPerGroup * S8) {
+      S = S8;
+      pl->claim = true;
+    }
+  }
   pl->splits = (int)S;
   pl->chunk = (int)chunk;
   if (S > 1) {
     const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
     pl->part_o_bytes = align256((size_t)S * rows * sv::kHeadDim * sizeof(float));
     pl->part_lse_bytes = align256((size_t)S * rows * sizeof(float));
+    pl->ws_bytes = kCounterBytes + pl->part_o_bytes + pl->part_lse_bytes;
   } else {
     pl->part_o_bytes = pl->part_lse_bytes = 0;
+    pl->ws_bytes = 0;
   }
-  pl->ws_bytes = pl->part_o_bytes + pl->part_lse_bytes;
   return ok();
 }
 
@@ -228,9 +247,11 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.q_start = q_start;
   a.out = static_cast<_Float16*>(out);
   a.out_lse = out_lse;
-  a.part_o = pl.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  a.part_lse = pl.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_o_bytes)
-                           : nullptr;
+  char* const ws = static_cast<char*>(workspace);
+  a.part_o = pl.ws_bytes ? reinterpret_cast<float*>(ws + kCounterBytes) : nullptr;
+  a.part_lse = pl.ws_bytes ? reinterpret_cast<float*>(ws + kCounterBytes + pl.part_o_bytes) : nullptr;
+  const bool claim = pl.claim && !q_start;
+  a.counters = claim ? reinterpret_cast<int32_t*>(ws) : nullptr;
   a.flags = status_flags;
   a.batch = p->batch;
   a.q_len = p->q_len;
@@ -248,7 +269,7 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.units = pl.splits * p->num_kv_heads * p->batch;
   a.window = p->window;
   a.sink = p->sink;
-  sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, s);
+  sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, claim, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
   if (pl.splits > 1) {
@@ -271,6 +292,9 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
     m.max_kv_len = p->max_kv_len;
     m.max_pages = p->max_pages_per_req;
     m.page_size = p->page_size;
+    m.counters = a.counters;
+    m.num_kv_heads = p->num_kv_heads;
+    m.flags = status_flags;
     sv::launch_merge(m, s);
     st = check_launch("verify_merge");
     if (st != SV_OK) return st;
@@ -319,6 +343,9 @@ sv_status sv_verify_merge(const float* part_o, const float* part_lse, int32_t nu
   m.out_lse = out_lse;
   m.kv_lens = nullptr;
   m.q_start = nullptr;
+  m.counters = nullptr;
+  m.num_kv_heads = 0;
+  m.flags = nullptr;
   m.batch = 0;
   m.window = 0;
   m.sink = 0;

@@ -708,9 +708,10 @@ struct Smem {
   static constexpr int BIG = RBYTES > OBYTES ? RBYTES : OBYTES;
 };
 
-template <int RB, bool FP8, int DEPTH, bool WIN>
+template <int RB, bool FP8, int DEPTH, bool WIN, bool CLAIM>
 __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   static_assert(DEPTH == 1 || DEPTH == 2, "one or two steps in flight");
+  static_assert(!CLAIM || (!FP8 && DEPTH == 1 && !WIN), "claimed work: fp16 KV, one step in flight, full attention");
   using SM = Smem<RB, FP8, DEPTH>;
   constexpr int NTS = kWavesPerGroup;  // waves that split the chunk's steps
   __shared__ __attribute__((aligned(1024))) unsigned char qsm[SM::QBYTES];
@@ -740,7 +741,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // evenly over the XCDs. For 2..64 requests ordered_unit takes the full
   // chunks in that order, then the last partial chunks, longest first.
   int split, g, b;
-  if (a.batch > 1 && a.batch <= kWave) {
+  if constexpr (CLAIM) {
+    // One request, S (a multiple of 8) workgroups per KV head: head
+    // (unit / 8) mod Hkv, so each head's workgroups sit on all 8 XCDs and
+    // the faster XCDs can claim more of its keys. `split` is the
+    // workgroup's partial slot.
+    const int grp = unit >> 3;
+    g = grp % a.num_kv_heads;
+    split = (grp / a.num_kv_heads) * 8 + (unit & 7);
+    b = 0;
+  } else if (a.batch > 1 && a.batch <= kWave) {
     if (!ordered_unit<WIN>(a, unit, lane, unit == 0 && rblk == 0 && tid < kWave, &split, &b, &g)) return;
   } else {
     const int hb = unit % (a.num_kv_heads * a.batch);
@@ -775,8 +785,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const int total = WIN ? live_steps(kv, L, W, S, &n_sink, &w0) : (kv > 0 ? (kv + kStep - 1) / kStep : 0);
   const int cs = a.chunk / kStep;
   const int n_chunks = total > 0 ? (total + cs - 1) / cs : 1;
-  if (split >= n_chunks) return;  // whole group: nothing of this request here
-  const bool direct = (n_chunks == 1);
+  if (!CLAIM && split >= n_chunks) return;  // whole group: nothing of this request here
+  const bool direct = !CLAIM && (n_chunks == 1);
   const int k_base = split * cs;
   const int n_steps = min(total - k_base, cs) > 0 ? min(total - k_base, cs) : 0;
   auto live_t0 = [&](int j) {
@@ -786,13 +796,49 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   };
   if (tid == 0) s_flag = 0;
 
-  const int my_steps = n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0;
   const int P = a.page_size, Hkv = a.num_kv_heads;
   const _Float16* kpool = static_cast<const _Float16*>(a.k_pages);
   const _Float16* vpool = static_cast<const _Float16*>(a.v_pages);
   const uint8_t* kpool8 = static_cast<const uint8_t*>(a.k_pages);
   const uint8_t* vpool8 = static_cast<const uint8_t*>(a.v_pages);
   const int32_t* ptab = a.page_table + (size_t)b * a.max_pages;
+  // cache row ((page, KV head, slot); the pool holds fewer than 2^32 rows)
+  // of position t whose page id is pid
+  auto row_of = [&](int pid, int t) -> uint32_t {
+    if (pid < 0 || pid >= a.num_pages) {
+      flag_bits |= 0x4;
+      pid = 0;
+    }
+    return ((uint32_t)pid * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
+  };
+  // Claimed work: this wave's first segment (the static one, or a first
+  // grain when the cache is too short for one) and the ticket of the next.
+  int c_f = 0, c_pool0 = 0, c_ngr = 0, seg_base = 0, seg_nb = 0, ticket1 = -1;
+  const int n_ctr = claim_counters(a.num_splits);
+  const int cidx = (ts + NTS * (split >> 3)) % n_ctr;  // this wave's counter of the head
+  int32_t* const ctr = CLAIM ? a.counters + (g * kClaimCounters + cidx) * kCounterStride : nullptr;
+  // pool grain of ticket t of this wave's counter (valid below c_ngr)
+  auto grain_of = [&](int t) { return cidx + t * n_ctr; };
+  if constexpr (CLAIM) {
+    claim_layout(total, a.num_splits, &c_f, &c_pool0, &c_ngr);
+    auto claim = [&]() {
+      int t = 0;
+      if (lane == 0) t = atomicAdd(ctr, 1);
+      return __builtin_amdgcn_readfirstlane(t);
+    };
+    if (c_f > 0) {
+      seg_base = (split * NTS + ts) * c_f;
+      seg_nb = c_f;
+    } else {
+      const int t0c = claim();
+      if (t0c >= 0 && grain_of(t0c) < c_ngr) {  // (a counter that did not start at 0 can give anything)
+        seg_base = c_pool0 + grain_of(t0c) * kGrain;
+        seg_nb = min(kGrain, total - seg_base);
+      }
+    }
+    if (seg_nb > 0) ticket1 = claim();
+  }
+  const int my_steps = CLAIM ? seg_nb : (n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0);
   // page id of each of the wave's steps bstart .. bstart+63, one per lane
   // Lane kl of the wave finds the cache row ((page, KV head, slot); the pool
   // holds fewer than 2^32 rows) of the first token of the wave's step
@@ -802,13 +848,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     uint32_t row = 0;
     const int kl = bstart + lane;
     if (kl < my_steps) {
-      const int t = live_t0(ts + kl * NTS);
-      int pid = ptab[t / P];
-      if (pid < 0 || pid >= a.num_pages) {
-        flag_bits |= 0x4;
-        pid = 0;
-      }
-      row = ((uint32_t)pid * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
+      const int t = CLAIM ? kStep * (seg_base + kl) : live_t0(ts + kl * NTS);
+      row = row_of(ptab[t / P], t);
     }
     return row;
   };
@@ -969,6 +1010,112 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
       ring_read8<63, 1024>(qa[rb], lds_addr(qf) + (uint32_t)(rb * 8 * kWave + lane) * 16u);
+    if constexpr (CLAIM) {
+      // Segments of consecutive steps (the static one, then claimed grains)
+      // run back to back through the one-step ring: during the first step
+      // of a segment that has a successor, the successor's page ids and the
+      // ticket of the segment after it are loaded, so the DMAs run on across
+      // segment ends without draining. A segment with a successor has at
+      // least 4 steps (only the last grain is shorter), so those rows are
+      // in registers before the step two from the end issues the first DMA
+      // of the successor.
+      const uint32_t ring_lds = lds_addr(ring);
+      constexpr int kWait = 8;
+      int base = seg_base, nb = my_steps, kk = 0;
+      uint32_t rows = rows_first;
+      int nbase = 0, nnb = 0;  // the successor (nnb 0: none)
+      if (ticket1 >= 0 && grain_of(ticket1) < c_ngr) {
+        nbase = c_pool0 + grain_of(ticket1) * kGrain;
+        nnb = min(kGrain, total - nbase);
+      }
+      uint32_t nrows = 0;
+      int tnext = -1;
+      // cache row of step j of the stream, counted from the current
+      // segment's first step; past the stream's end the last step again
+      auto tgt = [&](int j) -> size_t {
+        if (j < nb) return tok_row(rows, j);
+        if (nnb > 0) return tok_row(nrows, min(j - nb, nnb - 1));
+        return tok_row(rows, nb - 1);
+      };
+      if (nb > 0) {
+        half4_t pb[RB];
+        {
+          KFrag kf;
+          ring_read8<kWait, 64>(kf.k, ring_lds + k_lane_off(lane));
+          dma_k<0, 8>(kpool + tgt(1) * kHeadDim, ring, lane);
+          step_scores<RB>(kf, qa, ws, pb, lane, kStep * base, mk, a.scale_log2);
+        }
+        for (;;) {
+          if (kk + 1 >= nb && nnb == 0) break;  // step kk is the wave's last
+          const bool first = kk == 0 && nnb > 0;
+          const int t0 = kStep * (base + kk);
+          const int t1 = kk + 1 < nb ? t0 + kStep : kStep * nbase;
+          VFrag vf;
+          ring_read_vt<kWait>(vf, ring_lds + 8192 + v_lane_off(lane), lane);
+          // The successor's page ids and the next ticket, as plain vector
+          // loads the compiler does not wait for: the wait that follows 16
+          // DMAs later (below) completes them without draining the ring.
+          int pid_n = 0, tk = 0;
+          if (first) {
+            const int32_t* pp = ptab + kStep * (nbase + min(lane, nnb - 1)) / P;
+            asm volatile("global_load_dword %0, %1, off" : "+v"(pid_n) : "v"(pp) : "memory");
+            if (lane == 0) {
+              const int one = 1;
+              asm volatile("global_atomic_add %0, %1, %2, off sc0" : "+v"(tk) : "v"(ctr), "v"(one) : "memory");
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          dma_v<0, 8>(vpool + tgt(kk + 1) * kHeadDim, ring + 8192, lane);
+          KFrag kf;
+          // (two more operations are newer than K's DMAs after a first step)
+          if (first)
+            ring_read8_acc<kWait + 2, 64>(kf.k, ring_lds + k_lane_off(lane));
+          else
+            ring_read8_acc<kWait, 64>(kf.k, ring_lds + k_lane_off(lane));
+          dma_k<0, 8>(kpool + tgt(kk + 2) * kHeadDim, ring, lane);
+          float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
+          scores_mfma<RB>(kf, qa, a.scale_log2, x);
+          // (only the stream's last step can end above kv_len)
+          step_pv<RB, false>(vf, pb, ws, lane, t0, kv);
+          const bool any = mask_check<RB>(x, lmx, ws, mk, lane, t1);
+          softmax_p<RB>(x, ws, lsum, pb);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
+          if (any) {
+            move_ref<RB>(lmx, ws, alpha);
+            softmax_p<RB>(x, ws, lsum, pb);
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) ws.l[rb] = ws.l[rb] * alpha[rb] + lsum[rb];
+          if (any) rescale_o<RB>(ws, alpha);
+          __builtin_amdgcn_sched_barrier(0);
+          if (first) {
+            // exactly 16 DMAs (V and K of one step) were issued after the two
+            // loads: this completes them and leaves the DMAs in flight
+            asm volatile("s_waitcnt vmcnt(16)" : "+v"(pid_n), "+v"(tk) : : "memory");
+            nrows = row_of(pid_n, kStep * (nbase + min(lane, nnb - 1)));
+            tnext = __builtin_amdgcn_readfirstlane(tk);
+          }
+          if (++kk == nb) {
+            base = nbase;
+            nb = nnb;
+            rows = nrows;
+            kk = 0;
+            if (tnext >= 0 && grain_of(tnext) < c_ngr) {
+              nbase = c_pool0 + grain_of(tnext) * kGrain;
+              nnb = min(kGrain, total - nbase);
+            } else {
+              nnb = 0;
+            }
+            tnext = -1;
+          }
+        }
+        VFrag vf;
+        ring_read_vt<kWait>(vf, ring_lds + 8192 + v_lane_off(lane), lane);
+        step_pv<RB>(vf, pb, ws, lane, kStep * (base + kk), kv);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const uint32_t rows = bstart == 0 ? rows_first : step_rows(bstart);
       const int nb = min(kWave, my_steps - bstart);
@@ -1157,9 +1304,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
 template <bool FP8, int DEPTH, bool WIN>
 void launch_rb(const AttnArgs& a, int rb, dim3 grid, hipStream_t s) {
   const dim3 block(kThreads);
-  if (rb == 1 && DEPTH == 1) hipLaunchKernelGGL((verify_attn_kernel<1, FP8, 1, WIN>), grid, block, 0, s, a);
-  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, FP8, DEPTH, WIN>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((verify_attn_kernel<3, FP8, DEPTH, WIN>), grid, block, 0, s, a);
+  if (rb == 1 && DEPTH == 1) hipLaunchKernelGGL((verify_attn_kernel<1, FP8, 1, WIN, false>), grid, block, 0, s, a);
+  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, FP8, DEPTH, WIN, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((verify_attn_kernel<3, FP8, DEPTH, WIN, false>), grid, block, 0, s, a);
+}
+
+// claimed work: one request, fp16 KV, full attention, one row tile
+void launch_claim(const AttnArgs& a, int rb, hipStream_t s) {
+  const dim3 grid(a.units), block(kThreads);
+  if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false, 1, false, true>), grid, block, 0, s, a);
+  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false, 1, false, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((verify_attn_kernel<3, false, 1, false, true>), grid, block, 0, s, a);
 }
 
 template <bool FP8, bool WIN>
@@ -1172,9 +1327,11 @@ void launch_depth(const AttnArgs& a, int rb, hipStream_t s) {
     launch_rb<FP8, 1, WIN>(a, rb, dim3(a.units), s);
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, hipStream_t s) {
+void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, bool claim, hipStream_t s) {
   const bool win = a.window > 0;
-  if (fp8) {
+  if (claim) {
+    launch_claim(a, rb, s);
+  } else if (fp8) {
     if (win) launch_depth<true, true>(a, rb, s);
     else launch_depth<true, false>(a, rb, s);
   } else {

@@ -1,0 +1,98 @@
+"""GPU parity of claimed work against the float64 oracle: one request with
+fp16 keys whose split workgroups claim the keys in grains at run time (split
+count a multiple of 8, at least 64 key steps per wave). Covered: forced 8
+and 16 splits over a 40K cache (static first segments, then grains, a last
+grain that ends inside a page), the same plan over much shorter actual
+lengths (no static segment, a handful of grains for many waves, empty
+workgroups), one and two row blocks, agreement with the static split of the
+same call, repeated calls, and the work counters in the workspace's first
+32 KB (left zero by every call; a call on a workspace whose counters are not
+zero raises bit 0x10)."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import case, check, host, oracle, rows_of, run_gpu, say
+from long_context_gqa_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+KV = 40003  # >= 4096 * 8: claimed work with 8 splits; not a multiple of 16
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def plan(x, splits, max_kv):
+    c = B.VerifyCall(x.q, x.k_pages, x.v_pages, x.page_table.cuda().contiguous(), x.kv_lens.cuda(), x.wl.q_len,
+                     max_kv, None, None, x.sm_scale, splits)
+    return c
+
+
+@pytest.mark.parametrize("q_len,splits,variant", [(8, 8, "unit"), (8, 16, "literal"), (4, 8, "unit"),
+                                                  (1, 8, "unit")])
+def test_claimed_work_matches_oracle(q_len, splits, variant):
+    x = case(1, q_len, [KV], 16, variant, seed=40 + q_len + splits)
+    c = plan(x, splits, KV)
+    say(f"q={q_len} splits={splits} {variant}: plan {c.splits} x {c.chunk}")
+    assert c.splits == splits
+    out, lse, flags = run_gpu(x, num_splits=splits)
+    assert flags == 0
+    ref, ref_lse = oracle(x)
+    check(out, lse, ref, ref_lse, what=f"claimed q={q_len} S={splits}")
+    # the static split of the same call (7 splits: not a multiple of 8)
+    out7, lse7, flags7 = run_gpu(x, num_splits=7)
+    assert flags7 == 0
+    check(out7, lse7, ref, ref_lse, what="static S=7")
+    assert np.abs(out - out7).max() <= 2e-3
+
+
+@pytest.mark.parametrize("kv", [8, 9, 300, 1000, 4097, 20000])
+def test_claimed_work_over_shorter_actual_lengths(kv):
+    # the plan (8 splits, 40K) asks for claimed work; the request is shorter:
+    # below 4 * 32 * 4 = 512 steps there is no static segment, and only a few
+    # of the 32 waves per KV head get a grain
+    x = case(1, 8, [KV], 16, "unit", seed=9)
+    kvl = torch.tensor([kv], dtype=torch.int32)
+    out, lse, flags = run_gpu(x, num_splits=8, max_kv_len=KV, kv_lens=kvl)
+    assert flags == 0
+    h = host(x)
+    h["kv_lens"] = kvl
+    ref, ref_lse = oracle(x, h=h)
+    say(f"kv={kv}: max |err| {np.abs(out - ref).max():.2e}")
+    check(out, lse, ref, ref_lse, what=f"kv={kv}")
+
+
+def test_counters_left_zero_and_a_dirty_workspace_is_flagged():
+    x = case(1, 8, [KV], 16, "unit", seed=12)
+    c = plan(x, 8, KV)
+    ref, ref_lse = oracle(x, groups=[(0, 2)])
+    mask = rows_of(x, [(0, 2)])
+    outs = []
+    for i in range(3):
+        c.flags.zero_()
+        c.run()
+        torch.cuda.synchronize()
+        assert int(c.flags.item()) == 0
+        assert int(c.workspace[:32768].count_nonzero().item()) == 0
+        out = c.out.float().cpu().numpy()
+        check(out, c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask, what=f"call {i}")
+        outs.append(out)
+    # repeated calls agree to rounding (the grains' order varies)
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 2e-3
+    # a workspace whose counters are not zero: flagged, and cleared again
+    c.workspace[:4].fill_(3)
+    c.flags.zero_()
+    c.run()
+    torch.cuda.synchronize()
+    assert int(c.flags.item()) & 0x10
+    assert int(c.workspace[:32768].count_nonzero().item()) == 0
+    c.flags.zero_()
+    c.run()
+    torch.cuda.synchronize()
+    assert int(c.flags.item()) == 0
+    check(c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask, what="after the reset")
