@@ -32,6 +32,8 @@
 // the merge kernel. A workgroup holds at most 48 rows; a KV head with more is
 // covered by several workgroups (row tiles) that read the same keys, placed
 // on the same XCD so that the later reads are mostly served by its L2.
+#include <type_traits>
+
 #include "sv_common.h"
 
 namespace sv {
@@ -1215,50 +1217,70 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   }
 
   float* obuf = reinterpret_cast<float*>(bigsm);
-  for (int k = 0; k < NTS; ++k) {
-    if (ts == k) {
+  // Round r: wave w adds its quarter (w + r) mod 4 of the channels into the
+  // buffer (round 0 writes it), so every round has all four waves at work on
+  // disjoint quarters; each wave issues its quarter's LDS reads before the
+  // adds and writes.
+  static_assert(NTS == 4, "four waves, four channel quarters");
+  auto put = [&](auto qc, bool add) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr int N = RB * 4;  // float4 pieces of one quarter per lane
+    float4 val[N];
+    float4* dst[N];
+    int n = 0;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float* rowp = obuf + (rowbase + rb * 16 + lo) * kRowStride;
-        // O^T block j of lane (hi, lo) holds channel rows 4*hi + i of row lo:
-        // fp16 KV block j is channels 16j + 4*hi + i;
-        // FP8 KV block j = 4bb + c is channels 64bb + 4*(4*hi+i) + c
+    for (int rb = 0; rb < RB; ++rb) {
+      float* rowp = obuf + (rowbase + rb * 16 + lo) * kRowStride;
+      // O^T block j of lane (hi, lo) holds channel rows 4*hi + i of row lo:
+      // fp16 KV block j is channels 16j + 4*hi + i (blocks 8h + 2i and
+      // 8h + 2i + 1 fill channels of quarter 2h + i/2);
+      // FP8 KV block j = 4bb + c is channels 64bb + 4*(4*hi+i) + c (blocks
+      // 8h .. 8h + 3 of quarter 2h, blocks 8h + 4 .. 8h + 7 of quarter 2h + 1)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float4 v0, v1;
-            float* d0p;
-            float* d1p;
-            if constexpr (FP8) {
-              v0 = make_float4(ws.o[rb][8 * h + 0][i], ws.o[rb][8 * h + 1][i], ws.o[rb][8 * h + 2][i],
-                               ws.o[rb][8 * h + 3][i]);
-              v1 = make_float4(ws.o[rb][8 * h + 4][i], ws.o[rb][8 * h + 5][i], ws.o[rb][8 * h + 6][i],
-                               ws.o[rb][8 * h + 7][i]);
-              d0p = rowp + 64 * (2 * h) + 16 * hi + 4 * i;
-              d1p = rowp + 64 * (2 * h + 1) + 16 * hi + 4 * i;
-            } else {
-              // blocks j = 8h + 2i and 8h + 2i + 1
-              const int j0 = 8 * h + 2 * i;
-              v0 = make_float4(ws.o[rb][j0][0], ws.o[rb][j0][1], ws.o[rb][j0][2], ws.o[rb][j0][3]);
-              v1 = make_float4(ws.o[rb][j0 + 1][0], ws.o[rb][j0 + 1][1], ws.o[rb][j0 + 1][2], ws.o[rb][j0 + 1][3]);
-              d0p = rowp + 16 * j0 + 4 * hi;
-              d1p = d0p + 16;
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (FP8) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              if (2 * h + e == Q) {
+                const int j = 8 * h + 4 * e;
+                val[n] = make_float4(ws.o[rb][j][i], ws.o[rb][j + 1][i], ws.o[rb][j + 2][i], ws.o[rb][j + 3][i]);
+                dst[n++] = reinterpret_cast<float4*>(rowp + 64 * Q + 16 * hi + 4 * i);
+              }
             }
-            float4* q0 = reinterpret_cast<float4*>(d0p);
-            float4* q1 = reinterpret_cast<float4*>(d1p);
-            if (k == 0) {
-              *q0 = v0;
-              *q1 = v1;
-            } else {
-              const float4 a0 = *q0, a1 = *q1;
-              *q0 = make_float4(a0.x + v0.x, a0.y + v0.y, a0.z + v0.z, a0.w + v0.w);
-              *q1 = make_float4(a1.x + v1.x, a1.y + v1.y, a1.z + v1.z, a1.w + v1.w);
+          } else {
+            if (2 * h + i / 2 == Q) {
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int j = 8 * h + 2 * i + e;
+                val[n] = make_float4(ws.o[rb][j][0], ws.o[rb][j][1], ws.o[rb][j][2], ws.o[rb][j][3]);
+                dst[n++] = reinterpret_cast<float4*>(rowp + 16 * j + 4 * hi);
+              }
             }
           }
         }
       }
     }
+    if (add) {
+      float4 old[N];
+#pragma unroll
+      for (int k = 0; k < N; ++k) old[k] = *dst[k];
+#pragma unroll
+      for (int k = 0; k < N; ++k)
+        *dst[k] = make_float4(old[k].x + val[k].x, old[k].y + val[k].y, old[k].z + val[k].z, old[k].w + val[k].w);
+    } else {
+#pragma unroll
+      for (int k = 0; k < N; ++k) *dst[k] = val[k];
+    }
+  };
+  for (int r = 0; r < NTS; ++r) {
+    const int q = (ts + r) & 3;
+    const bool add = r > 0;
+    if (q == 0) put(std::integral_constant<int, 0>{}, add);
+    else if (q == 1) put(std::integral_constant<int, 1>{}, add);
+    else if (q == 2) put(std::integral_constant<int, 2>{}, add);
+    else put(std::integral_constant<int, 3>{}, add);
     __syncthreads();
   }
 
