@@ -775,7 +775,46 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   if (row0 >= R) return;  // a narrow block leaves the last row tiles empty
   const size_t split_stride = (size_t)a.batch * a.q_len * Hq;  // rows of one split's partials
 
-  const int raw_kv = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
+  // Q fragments of the workgroup's rows, in MFMA B-operand order: loaded into
+  // registers first (they depend on no length), so that their latency
+  // overlaps the length, page and first K/V loads; they go to LDS once the
+  // first DMAs are out.
+  constexpr int kQPer = RB * 8 * kWave / kThreads;
+  u32x4 qv[kQPer];
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int idx = tid + k * kThreads;
+    const int frag = idx / kWave, ln = idx % kWave;
+    const int rb = frag / 8, s = frag % 8;
+    const int r = row0 + rb * 16 + (ln & 15);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R) {
+      const int i = r / G, j = r % G;
+      // channel map of the score MFMA's k-step s: fp16 KV 32s + 8*(lane/16);
+      // FP8 KV 64*(s/2) + 16*(lane/16) + 8*(s%2) (two k-steps per scale block)
+      const int d0 = FP8 ? 64 * (s >> 1) + 16 * (ln >> 4) + 8 * (s & 1) : 32 * s + 8 * (ln >> 4);
+      const _Float16* src = a.q + ((size_t)(rstart + i) * Hq + g * G + j) * kHeadDim + d0;
+      v = *reinterpret_cast<const u32x4*>(src);
+    }
+    qv[k] = v;
+  }
+
+  const int raw_kv_v = a.kv_lens[b];
+  // claimed work: this wave's counter of the head, and its first ticket (of
+  // its second segment, or of its first when the cache is too short for a
+  // static one), which does not depend on the length either
+  const int n_ctr = claim_counters(a.num_splits);
+  const int cidx = (ts + NTS * (split >> 3)) % n_ctr;
+  int32_t* const ctr = CLAIM ? a.counters + (g * kClaimCounters + cidx) * kCounterStride : nullptr;
+  // pool grain of ticket t of this wave's counter (valid below c_ngr)
+  auto grain_of = [&](int t) { return cidx + t * n_ctr; };
+  int first_ticket = -1;
+  if constexpr (CLAIM) {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(ctr, 1);
+    first_ticket = __builtin_amdgcn_readfirstlane(t);
+  }
+  const int raw_kv = __builtin_amdgcn_readfirstlane(raw_kv_v);
   const int kv = clamp_kv_len(raw_kv, a.max_kv_len, a.max_pages, a.page_size, &flag_bits);
   if (raw_kv < q_len) flag_bits |= 0x2;
   const int L = kv - q_len;
@@ -816,11 +855,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // Claimed work: this wave's first segment (the static one, or a first
   // grain when the cache is too short for one) and the ticket of the next.
   int c_f = 0, c_pool0 = 0, c_ngr = 0, seg_base = 0, seg_nb = 0, ticket1 = -1;
-  const int n_ctr = claim_counters(a.num_splits);
-  const int cidx = (ts + NTS * (split >> 3)) % n_ctr;  // this wave's counter of the head
-  int32_t* const ctr = CLAIM ? a.counters + (g * kClaimCounters + cidx) * kCounterStride : nullptr;
-  // pool grain of ticket t of this wave's counter (valid below c_ngr)
-  auto grain_of = [&](int t) { return cidx + t * n_ctr; };
   if constexpr (CLAIM) {
     claim_layout(total, a.num_splits, &c_f, &c_pool0, &c_ngr);
     auto claim = [&]() {
@@ -831,14 +865,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     if (c_f > 0) {
       seg_base = (split * NTS + ts) * c_f;
       seg_nb = c_f;
+      ticket1 = first_ticket;
     } else {
-      const int t0c = claim();
+      const int t0c = first_ticket;
       if (t0c >= 0 && grain_of(t0c) < c_ngr) {  // (a counter that did not start at 0 can give anything)
         seg_base = c_pool0 + grain_of(t0c) * kGrain;
         seg_nb = min(kGrain, total - seg_base);
+        ticket1 = claim();
       }
     }
-    if (seg_nb > 0) ticket1 = claim();
   }
   const int my_steps = CLAIM ? seg_nb : (n_steps > ts ? (n_steps - ts + NTS - 1) / NTS : 0);
   // page id of each of the wave's steps bstart .. bstart+63, one per lane
@@ -881,23 +916,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
     }
   }
 
-  // Q fragments of the workgroup's rows into LDS, in MFMA B-operand order.
+  // the Q fragments (loaded above) into LDS
   u32x4* qlds = reinterpret_cast<u32x4*>(qsm);
-  for (int idx = tid; idx < RB * 8 * kWave; idx += kThreads) {
-    const int frag = idx / kWave, ln = idx % kWave;
-    const int rb = frag / 8, s = frag % 8;
-    const int r = row0 + rb * 16 + (ln & 15);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < R) {
-      const int i = r / G, j = r % G;
-      // channel map of the score MFMA's k-step s: fp16 KV 32s + 8*(lane/16);
-      // FP8 KV 64*(s/2) + 16*(lane/16) + 8*(s%2) (two k-steps per scale block)
-      const int d0 = FP8 ? 64 * (s >> 1) + 16 * (ln >> 4) + 8 * (s & 1) : 32 * s + 8 * (ln >> 4);
-      const _Float16* src = a.q + ((size_t)(rstart + i) * Hq + g * G + j) * kHeadDim + d0;
-      v = *reinterpret_cast<const u32x4*>(src);
-    }
-    qlds[idx] = v;
-  }
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) qlds[tid + k * kThreads] = qv[k];
   __syncthreads();
 
   WaveState<RB> ws;
