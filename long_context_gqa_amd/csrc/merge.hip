@@ -114,6 +114,70 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const float* lse = a.part_lse + item;
   const float* po = a.part_o + item * a.head_dim;
 
+  // Up to 64 splits of 256 channels (every launch of the verify entry point
+  // with a workgroup per item): wave w takes splits w, w + 4, ..., lane l
+  // channels 4l..4l+3, and every load goes out at once (one round trip);
+  // the split maximum and the sums meet in LDS.
+  constexpr int kPer = 16;
+  if (S <= kWavesPerGroup * kPer && a.head_dim == 4 * kWave) {
+    float lv[kPer];
+    float4 ov[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int s = w + kWavesPerGroup * k;
+      lv[k] = -INFINITY;
+      ov[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < S) {
+        lv[k] = lse[s * sl];
+        ov[k] = reinterpret_cast<const float4*>(po + s * so)[lane];
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) m = fmaxf(m, lv[k]);
+    if (lane == 0) red[w] = m;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int k = 1; k < kWavesPerGroup; ++k) M = fmaxf(M, red[k]);
+    const float ref = (M == -INFINITY) ? 0.f : M;
+    float t = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const float wgt = (lv[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((lv[k] - ref) * kLog2e);
+      t += wgt;
+      acc.x += wgt * ov[k].x;
+      acc.y += wgt * ov[k].y;
+      acc.z += wgt * ov[k].z;
+      acc.w += wgt * ov[k].w;
+    }
+    __syncthreads();  // every wave has read red
+    if (lane == 0) red[w] = t;
+    if (w > 0) acc_s[w - 1][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+      float tot = red[0];
+#pragma unroll
+      for (int k = 1; k < kWavesPerGroup; ++k) {
+        tot += red[k];
+        const float4 u = acc_s[k - 1][lane];
+        acc.x += u.x;
+        acc.y += u.y;
+        acc.z += u.z;
+        acc.w += u.w;
+      }
+      const float inv = tot > 0.f ? 1.f / tot : 0.f;
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      h4 hv = {(_Float16)(acc.x * inv), (_Float16)(acc.y * inv), (_Float16)(acc.z * inv),
+               (_Float16)(acc.w * inv)};
+      reinterpret_cast<h4*>(a.out + item * a.head_dim)[lane] = hv;
+      if (a.out_lse && lane == 0)
+        a.out_lse[item] = tot > 0.f ? ref + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+
   float mx = -INFINITY;
   for (int s = threadIdx.x; s < S; s += kThreads) mx = fmaxf(mx, lse[s * sl]);
   mx = block_reduce(mx, red, true);

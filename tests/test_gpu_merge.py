@@ -21,6 +21,9 @@ def _gpu():
 
 @pytest.mark.parametrize("S,R,H,D", [(1, 3, 2, 256), (5, 4, 3, 100), (130, 2, 24, 256), (17, 3, 2, 1024),
                                      (300, 1, 1, 4), (300, 2, 1, 4),
+                                     # up to 64 splits of 256 channels: every load in one round trip
+                                     (64, 8, 24, 256), (63, 2, 3, 256), (33, 8, 24, 256), (2, 5, 24, 256),
+                                     (65, 2, 3, 256),
                                      # 4,096 and more (row, head) items: one wave per item
                                      (7, 200, 24, 256), (20, 171, 24, 256), (3, 4096, 1, 100), (1, 512, 24, 256)])
 def test_merge_matches_oracle(S, R, H, D):
