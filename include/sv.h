@@ -141,12 +141,13 @@ sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t
  *
  * Arithmetic: fp16 (or exactly dequantised E4M3) inputs, fp32 accumulation;
  * the result does not depend on the number of splits beyond rounding.
- * Repeated calls give the same bits, except for one request with fp16 keys,
- * full attention, q_len*Hq/Hkv <= 48, a split count that is a multiple of 8
- * and max_kv_len >= 4096 * splits (at least 64 key steps of 16 per wave;
- * e.g. 256K tokens at the automatic 64 splits): there the waves of each KV
- * head claim 64-key grains at run time, so the order of the softmax
- * updates, and with it the rounding, varies between calls.
+ * Repeated calls give the same bits, except with fp16 keys, full attention,
+ * q_len*Hq/Hkv <= 48, a split count that is a multiple of 8, at most 128
+ * (request, KV head) groups and max_kv_len >= 4096 * splits (at least 64 key
+ * steps of 16 per wave; e.g. 256K tokens at the automatic 64 splits of one
+ * request, 32K at the 8 splits of 8 requests): there the waves of each group
+ * claim 64-key grains at run time, so the order of the softmax updates, and
+ * with it the rounding, varies between calls.
  */
 sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const void* k_pages,
                               const void* v_pages, const void* k_scales, const void* v_scales,

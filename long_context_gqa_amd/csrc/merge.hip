@@ -86,15 +86,17 @@ __device__ __forceinline__ int item_splits(const MergeArgs& a, int row) {
 // left at zero for the next call. Runs once, in block 0, after the attention
 // kernel has finished.
 __device__ __forceinline__ void settle_counters(const MergeArgs& a) {
-  if (!a.counters || blockIdx.x != 0 || (int)threadIdx.x >= a.num_kv_heads * kClaimCounters) return;
+  const int groups = a.batch * a.num_kv_heads;
+  const int C = a.counters ? claim_counters(a.num_splits, groups) : 1;
+  if (!a.counters || blockIdx.x != 0 || (int)threadIdx.x >= groups * C) return;
+  const int q = (int)threadIdx.x / C, c = (int)threadIdx.x % C;  // group q = b * Hkv + g
   int dummy = 0;
-  const int kv = clamp_kv_len(a.kv_lens[0], a.max_kv_len, a.max_pages, a.page_size, &dummy);
+  const int kv = clamp_kv_len(a.kv_lens[q / a.num_kv_heads], a.max_kv_len, a.max_pages, a.page_size, &dummy);
   int f, pool0, n_grains;
   claim_layout(kv > 0 ? (kv + 15) / 16 : 0, a.num_splits, &f, &pool0, &n_grains);
   // counter c of C deals its grains to S / 2 / C * 8 waves, each of which
-  // fails once; counters past C are not used
-  const int C = claim_counters(a.num_splits), c = (int)threadIdx.x % kClaimCounters;
-  const int want = c < C ? counter_grains(n_grains, c, C) + a.num_splits / 2 / C * 8 : 0;
+  // fails once
+  const int want = counter_grains(n_grains, c, C) + a.num_splits / 2 / C * 8;
   int32_t* const ctr = a.counters + threadIdx.x * kCounterStride;
   if (*ctr != want && a.flags) atomicOr(a.flags, 0x10);
   *ctr = 0;

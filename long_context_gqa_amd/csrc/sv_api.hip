@@ -58,7 +58,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct Plan {
   int rb, row_blocks;  // row blocks of 16 per workgroup; workgroups per (chunk, KV head, request)
   int splits, chunk;   // key chunks and their length in tokens
-  bool claim;          // one request: its KV heads' keys are claimed in grains (splits = slots per head)
+  bool claim;          // the keys of each (request, KV head) are claimed in grains (splits = slots per group)
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
 
@@ -162,13 +162,14 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   S = (maxkv + chunk - 1) / chunk;
   if (S * p->num_kv_heads * p->batch * 2 * rgs > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "too many workgroups (%lld splits)", S);
-  // One long request with fp16 keys, full attention and one row tile: its
-  // workgroups (S a multiple of 8, so every KV head has workgroups on all 8
-  // XCDs) claim the keys in grains, which evens out XCDs that stream at
-  // different rates. Only where every wave has about 64 steps or more.
+  // Long caches with fp16 keys, full attention, blocks of one width and one
+  // row tile: the workgroups of each (request, KV head) group (S a multiple
+  // of 8, so every group has workgroups on all 8 XCDs) claim its keys in
+  // grains, which evens out XCDs that stream at different rates. Only where
+  // every wave has about 64 steps or more, and every group's counters fit.
   pl->claim = false;
-  if (p->batch == 1 && p->window == 0 && p->kv_dtype == SV_KV_FP16 && pl->row_blocks == 1 &&
-      p->num_kv_heads * sv::kClaimCounters <= sv::kCounterSlots) {
+  if (p->window == 0 && p->kv_dtype == SV_KV_FP16 && pl->row_blocks == 1 &&
+      (long long)p->batch * p->num_kv_heads <= sv::kCounterSlots) {
     const long long S8 = p->num_splits > 0 ? S : (S + 7) / 8 * 8;
     if (S8 >= 8 && S8 % 8 == 0 && (maxkv + 15) / 16 >= 64LL * sv::kWavesPerGroup * S8) {
       S = S8;

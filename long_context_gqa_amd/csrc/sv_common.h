@@ -40,7 +40,7 @@ struct AttnArgs {
   int32_t units;       // num_splits * num_kv_heads * batch, numbered split-major
   int32_t window, sink;  // sliding window (0: full attention) and leading sink positions
   float scale_log2;  // sm_scale * log2(e)
-  int32_t* counters;  // grain counters, one per KV head (claimed work: one request, split keys)
+  int32_t* counters;  // claimed work: the grain counters of every (request, KV head) group
 };
 
 struct MergeArgs {
@@ -53,9 +53,8 @@ struct MergeArgs {
   int32_t num_splits, num_rows, num_heads, head_dim;
   int32_t q_len, chunk, max_kv_len, max_pages, page_size, batch;
   int32_t window, sink;  // as in AttnArgs (the chunks tile the block's live key steps)
-  // claimed work (one request): the grain counters to check and clear, one
-  // per KV head (NULL otherwise), and the flag word for a counter that did
-  // not start at zero
+  // claimed work: the grain counters to check and clear (NULL otherwise),
+  // and the flag word for a counter that did not start at zero
   int32_t* counters;
   int32_t num_kv_heads;
   int32_t* flags;
@@ -114,36 +113,38 @@ __device__ inline int live_steps(int kv, int L, int window, int sink, int* n_sin
   return ns + (kv > w0 ? (kv - w0 + 15) / 16 : 0);
 }
 
-// Claimed work for one request whose keys are split over S workgroups per KV
-// head (4 waves each): wave w of workgroup s first takes the static segment
-// of steps [(4s + w) * f, (4s + w + 1) * f), f up to 64 (about three quarters
-// of the steps over all waves, 0 for short caches); the steps from
-// pool0 = 4 * S * f on form grains of kGrain steps that the waves of the head
-// claim one at a time from the head's counter (grain index = ticket). Every
-// wave stops after its first ticket past the last grain, so a head's counter
-// ends at n_grains + 4 * S: the merge checks that and clears it.
+// Claimed work for a (request, KV head) group whose keys are split over S
+// workgroups (4 waves each): wave w of workgroup s first takes the static
+// segment of steps [(4s + w) * f, (4s + w + 1) * f), f up to 64 (about three
+// quarters of the steps over all waves, 0 for short caches); the steps from
+// pool0 = 4 * S * f on form grains of kGrain steps that the group's waves
+// claim one at a time from its counters (below). Every wave stops after its
+// first ticket past its counter's last grain, so each counter ends at its
+// grain count plus its wave count: the merge checks that and clears it.
 #ifndef SV_GRAIN
 #define SV_GRAIN 4
 #endif
 constexpr int kGrain = SV_GRAIN;
-// Each KV head's grains are dealt over C counters (grain c + k * C is ticket
-// k of counter c), so that no one address takes every claim of the head. C is
-// the largest power of two up to kClaimCounters that divides S / 2; wave w of
+// Each (request, KV head) group's grains are dealt over C counters (grain
+// c + k * C is ticket k of counter c), so that no one address takes every
+// claim of the group. C is the largest power of two up to kClaimCounters that
+// divides S / 2 and leaves room for every group's counters; wave w of
 // workgroup slot s claims from counter (w + 4 * (s / 8)) mod C. Slots s and
 // s + 1 .. s + 7 sit on the 8 different XCDs, so every counter's waves are
-// spread over all XCDs, S / 2 / C * 8 of them per counter.
+// spread over all XCDs, S / 2 / C * 8 of them per counter. Counter c of group
+// q sits in slot q * C + c.
 #ifndef SV_CTRS
 #define SV_CTRS 16
 #endif
 constexpr int kClaimCounters = SV_CTRS;
-__host__ __device__ inline int claim_counters(int splits) {
+constexpr int kCounterSlots = 128;
+__host__ __device__ inline int claim_counters(int splits, int groups) {
   int c = kClaimCounters;
-  while (c > 1 && (splits / 2) % c != 0) c /= 2;
+  while (c > 1 && ((splits / 2) % c != 0 || c * groups > kCounterSlots)) c /= 2;
   return c;
 }
 // each counter on its own 256-byte line (int32 stride), in a block of 32 KB
 constexpr int kCounterStride = 64;
-constexpr int kCounterSlots = 128;
 // the number of grains counter c of C deals
 __device__ inline int counter_grains(int n_grains, int c, int C) {
   return n_grains > c ? (n_grains - c + C - 1) / C : 0;

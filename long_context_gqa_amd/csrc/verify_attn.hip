@@ -744,14 +744,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // chunks in that order, then the last partial chunks, longest first.
   int split, g, b;
   if constexpr (CLAIM) {
-    // One request, S (a multiple of 8) workgroups per KV head: head
-    // (unit / 8) mod Hkv, so each head's workgroups sit on all 8 XCDs and
-    // the faster XCDs can claim more of its keys. `split` is the
+    // S (a multiple of 8) workgroups per (request, KV head) group: group
+    // (unit / 8) mod (B * Hkv), so each group's workgroups sit on all 8 XCDs
+    // and the faster XCDs can claim more of its keys. `split` is the
     // workgroup's partial slot.
-    const int grp = unit >> 3;
-    g = grp % a.num_kv_heads;
-    split = (grp / a.num_kv_heads) * 8 + (unit & 7);
-    b = 0;
+    const int grp = unit >> 3, n_grp = a.batch * a.num_kv_heads;
+    g = (grp % n_grp) % a.num_kv_heads;
+    b = (grp % n_grp) / a.num_kv_heads;
+    split = (grp / n_grp) * 8 + (unit & 7);
   } else if (a.batch > 1 && a.batch <= kWave) {
     if (!ordered_unit<WIN>(a, unit, lane, unit == 0 && rblk == 0 && tid < kWave, &split, &b, &g)) return;
   } else {
@@ -803,9 +803,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // claimed work: this wave's counter of the head, and its first ticket (of
   // its second segment, or of its first when the cache is too short for a
   // static one), which does not depend on the length either
-  const int n_ctr = claim_counters(a.num_splits);
+  const int n_ctr = claim_counters(a.num_splits, a.batch * a.num_kv_heads);
   const int cidx = (ts + NTS * (split >> 3)) % n_ctr;
-  int32_t* const ctr = CLAIM ? a.counters + (g * kClaimCounters + cidx) * kCounterStride : nullptr;
+  int32_t* const ctr = CLAIM ? a.counters + ((b * a.num_kv_heads + g) * n_ctr + cidx) * kCounterStride : nullptr;
   // pool grain of ticket t of this wave's counter (valid below c_ngr)
   auto grain_of = [&](int t) { return cidx + t * n_ctr; };
   int first_ticket = -1;
@@ -1353,7 +1353,7 @@ void launch_rb(const AttnArgs& a, int rb, dim3 grid, hipStream_t s) {
   else hipLaunchKernelGGL((verify_attn_kernel<3, FP8, DEPTH, WIN, false>), grid, block, 0, s, a);
 }
 
-// claimed work: one request, fp16 KV, full attention, one row tile
+// claimed work: fp16 KV, full attention, one row tile, blocks of one width
 void launch_claim(const AttnArgs& a, int rb, hipStream_t s) {
   const dim3 grid(a.units), block(kThreads);
   if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false, 1, false, true>), grid, block, 0, s, a);

@@ -96,3 +96,17 @@ def test_counters_left_zero_and_a_dirty_workspace_is_flagged():
     torch.cuda.synchronize()
     assert int(c.flags.item()) == 0
     check(c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask, what="after the reset")
+
+
+@pytest.mark.parametrize("lens,splits", [([KV] * 3, 8), ([KV, 9000, 300, KV - 20, 17], 8), ([70000, 70000], 16)])
+def test_claimed_work_over_a_batch(lens, splits):
+    # uniform blocks over several requests: a group per (request, KV head),
+    # each with its own counters (ragged lengths are correct, only slower)
+    x = case(len(lens), 8, lens, 16, "unit", seed=len(lens) + splits)
+    c = plan(x, splits, max(lens))
+    say(f"batch {len(lens)} lens {lens} splits {splits}: plan {c.splits} x {c.chunk}")
+    out, lse, flags = run_gpu(x, num_splits=splits)
+    assert flags == 0
+    groups = [(b, g) for b in range(len(lens)) for g in (0, 3)]
+    ref, ref_lse = oracle(x, groups=groups)
+    check(out, lse, ref, ref_lse, mask=rows_of(x, groups), what=f"batch {len(lens)}")
