@@ -1,5 +1,5 @@
-"""GPU parity of claimed work against the float64 oracle: one request with
-fp16 keys whose split workgroups claim the keys in grains at run time (split
+"""GPU parity of claimed work against the float64 oracle: requests with fp16
+keys whose split workgroups claim the keys in grains at run time (split
 count a multiple of 8, at least 64 key steps per wave). Covered: forced 8
 and 16 splits over a 40K cache (static first segments, then grains, a last
 grain that ends inside a page), the same plan over much shorter actual
@@ -28,7 +28,7 @@ def _gpu():
 
 def plan(x, splits, max_kv):
     c = B.VerifyCall(x.q, x.k_pages, x.v_pages, x.page_table.cuda().contiguous(), x.kv_lens.cuda(), x.wl.q_len,
-                     max_kv, None, None, x.sm_scale, splits)
+                     max_kv, x.k_scales, x.v_scales, x.sm_scale, splits)
     return c
 
 
@@ -110,3 +110,4 @@ def test_claimed_work_over_a_batch(lens, splits):
     groups = [(b, g) for b in range(len(lens)) for g in (0, 3)]
     ref, ref_lse = oracle(x, groups=groups)
     check(out, lse, ref, ref_lse, mask=rows_of(x, groups), what=f"batch {len(lens)}")
+
