@@ -111,3 +111,17 @@ def test_claimed_work_over_a_batch(lens, splits):
     ref, ref_lse = oracle(x, groups=groups)
     check(out, lse, ref, ref_lse, mask=rows_of(x, groups), what=f"batch {len(lens)}")
 
+
+
+@pytest.mark.parametrize("page,q_len,Hq,Hkv", [(64, 8, 24, 4), (48, 8, 24, 4), (16, 16, 24, 8), (32, 4, 16, 8)])
+def test_claimed_work_pages_and_heads(page, q_len, Hq, Hkv):
+    # steps of 16 positions inside larger pages (48: not a power of two), and
+    # 8 KV heads (three or two query heads each; 48 or 8 rows per KV head)
+    x = case(1, q_len, [KV], page, "unit", seed=page + q_len + Hkv, Hq=Hq, Hkv=Hkv)
+    c = plan(x, 8, KV)
+    say(f"P={page} q={q_len} Hq={Hq} Hkv={Hkv}: plan {c.splits} x {c.chunk}")
+    out, lse, flags = run_gpu(x, num_splits=8)
+    assert flags == 0
+    groups = [(0, 0), (0, Hkv - 1)]
+    ref, ref_lse = oracle(x, groups=groups)
+    check(out, lse, ref, ref_lse, mask=rows_of(x, groups), what=f"P={page} Hkv={Hkv}")
