@@ -121,10 +121,7 @@ __device__ inline int live_steps(int kv, int L, int window, int sink, int* n_sin
 // claim one at a time from its counters (below). Every wave stops after its
 // first ticket past its counter's last grain, so each counter ends at its
 // grain count plus its wave count: the merge checks that and clears it.
-#ifndef SV_GRAIN
-#define SV_GRAIN 4
-#endif
-constexpr int kGrain = SV_GRAIN;
+constexpr int kGrain = 4;
 // Each (request, KV head) group's grains are dealt over C counters (grain
 // c + k * C is ticket k of counter c), so that no one address takes every
 // claim of the group. C is the largest power of two up to kClaimCounters that
@@ -133,10 +130,7 @@ constexpr int kGrain = SV_GRAIN;
 // s + 1 .. s + 7 sit on the 8 different XCDs, so every counter's waves are
 // spread over all XCDs, S / 2 / C * 8 of them per counter. Counter c of group
 // q sits in slot q * C + c.
-#ifndef SV_CTRS
-#define SV_CTRS 16
-#endif
-constexpr int kClaimCounters = SV_CTRS;
+constexpr int kClaimCounters = 16;
 constexpr int kCounterSlots = 128;
 __host__ __device__ inline int claim_counters(int splits, int groups) {
   int c = kClaimCounters;
