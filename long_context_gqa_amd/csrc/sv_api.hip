@@ -162,14 +162,16 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   S = (maxkv + chunk - 1) / chunk;
   if (S * p->num_kv_heads * p->batch * 2 * rgs > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "too many workgroups (%lld splits)", S);
-  // Long caches with fp16 keys, full attention, blocks of one width and one
-  // row tile: the workgroups of each (request, KV head) group (S a multiple
-  // of 8, so every group has workgroups on all 8 XCDs) claim its keys in
-  // grains, which evens out XCDs that stream at different rates. Only where
-  // every wave has about 64 steps or more, and every group's counters fit.
+  // One long request with fp16 keys, full attention and one row tile: the
+  // workgroups of each KV head (S a multiple of 8, so every head has
+  // workgroups on all 8 XCDs) claim its keys in grains, which evens out XCDs
+  // that stream at different rates. Only where every wave has about 64 steps
+  // or more. Batches keep the static order: their lengths may be ragged
+  // (only the device knows), and there the longest-first order of fixed
+  // chunks beats an equal number of workgroups per request.
   pl->claim = false;
-  if (p->window == 0 && p->kv_dtype == SV_KV_FP16 && pl->row_blocks == 1 &&
-      (long long)p->batch * p->num_kv_heads <= sv::kCounterSlots) {
+  if (p->batch == 1 && p->window == 0 && p->kv_dtype == SV_KV_FP16 && pl->row_blocks == 1 &&
+      p->num_kv_heads <= sv::kCounterSlots) {
     const long long S8 = p->num_splits > 0 ? S : (S + 7) / 8 * 8;
     if (S8 >= 8 && S8 % 8 == 0 && (maxkv + 15) / 16 >= 64LL * sv::kWavesPerGroup * S8) {
       S = S8;

@@ -99,14 +99,21 @@ def test_counters_left_zero_and_a_dirty_workspace_is_flagged():
 
 
 @pytest.mark.parametrize("lens,splits", [([KV] * 3, 8), ([KV, 9000, 300, KV - 20, 17], 8), ([70000, 70000], 16)])
-def test_claimed_work_over_a_batch(lens, splits):
-    # uniform blocks over several requests: a group per (request, KV head),
-    # each with its own counters (ragged lengths are correct, only slower)
+def test_batches_keep_the_static_order(lens, splits):
+    # several requests never claim (their lengths may be ragged): the same
+    # plans as above over batches are exact against the oracle and, in the
+    # static order, give the same bits on every call
     x = case(len(lens), 8, lens, 16, "unit", seed=len(lens) + splits)
     c = plan(x, splits, max(lens))
     say(f"batch {len(lens)} lens {lens} splits {splits}: plan {c.splits} x {c.chunk}")
     out, lse, flags = run_gpu(x, num_splits=splits)
     assert flags == 0
+    c.run()
+    torch.cuda.synchronize()
+    first = c.out.clone()
+    c.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first, c.out)
     groups = [(b, g) for b in range(len(lens)) for g in (0, 3)]
     ref, ref_lse = oracle(x, groups=groups)
     check(out, lse, ref, ref_lse, mask=rows_of(x, groups), what=f"batch {len(lens)}")
