@@ -50,7 +50,9 @@ def test_claimed_work_matches_oracle(q_len, splits, variant):
     assert np.abs(out - out7).max() <= 2e-3
 
 
-@pytest.mark.parametrize("kv", [8, 9, 300, 1000, 4097, 20000])
+# 2720 / 2736 / 2737: 170 / 171 / 172 steps, where a wave's static segment
+# goes from none (all 170 steps claimed) to 4 steps, the last one partial
+@pytest.mark.parametrize("kv", [8, 9, 300, 1000, 2720, 2736, 2737, 4097, 20000])
 def test_claimed_work_over_shorter_actual_lengths(kv):
     # the plan (8 splits, 40K) asks for claimed work; the request is shorter:
     # below 4 * 32 * 4 = 512 steps there is no static segment, and only a few
