@@ -134,3 +134,34 @@ def test_claimed_work_pages_and_heads(page, q_len, Hq, Hkv):
     groups = [(0, 0), (0, Hkv - 1)]
     ref, ref_lse = oracle(x, groups=groups)
     check(out, lse, ref, ref_lse, mask=rows_of(x, groups), what=f"P={page} Hkv={Hkv}")
+
+
+def test_claimed_work_replays_in_a_graph():
+    # the counters must be back at zero after every replay (the merge clears
+    # them with plain stores inside the graph); each replay, with an eager
+    # call between, is checked against the oracle and must raise no flag
+    x = case(1, 8, [KV], 16, "unit", seed=21)
+    c = plan(x, 8, KV)
+    ref, ref_lse = oracle(x, groups=[(0, 1)])
+    mask = rows_of(x, [(0, 1)])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            c.flags.zero_()
+            c.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        c.flags.zero_()
+        c.run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(c.flags.item()) == 0
+        assert int(c.workspace[:32768].count_nonzero().item()) == 0
+        check(c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask, what=f"replay {r}")
+        out2, lse2, flags2 = run_gpu(x, num_splits=8)  # eager work between replays
+        assert flags2 == 0
