@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--extend", default=None,
                     help="also time extend chunks of these widths (comma list, up to 512 rows per request) "
                          "over the workload's cache, against the fp16 MFMA peak")
+    ap.add_argument("--claim", action="store_true",
+                    help="also time the opt-in claimed-work mode (SV_VERIFY_CLAIMED_WORK; reproducible to rounding "
+                         "only) against the default plan, alternating the two")
     ap.add_argument("--traffic", default=None,
                     help="JSON with measured HBM bytes per verify_attn launch (default: the one under "
                          "profiles/ for this workload, used only while the kernel source is unchanged)")
@@ -246,6 +249,24 @@ def main():
                     "note": "device copy (read + write) as an attainable-bandwidth reference"}
         del src, dst
 
+    claimed = None
+    if args.claim:
+        cc = B.VerifyCall(x.q, x.k_pages, x.v_pages, page_table, kv_lens, wl.q_len, x.max_kv_len, x.k_scales,
+                          x.v_scales, x.sm_scale, args.splits, claim=True)
+        for _ in range(3):
+            cc.run(stream)
+        # alternate the two modes in rounds, so that drift over the run hits both alike
+        us_c, us_d = [], []
+        for _ in range(5):
+            us_c.append(timed(lambda: cc.run(stream), n_part))
+            us_d.append(timed(lambda: call.run(stream), n_part))
+        uc, ud = float(np.median(np.concatenate(us_c))), float(np.median(np.concatenate(us_d)))
+        claimed = {"us_median": round(uc, 2), "GBps": round(attn_bytes / (uc * 1e-6) / 1e9, 1),
+                   "default_us_median": round(ud, 2), "default_GBps": round(attn_bytes / (ud * 1e-6) / 1e9, 1),
+                   "splits": cc.splits, "flags": int(cc.flags.item())}
+        log(f"[bench] claimed work {uc:.2f} us vs default {ud:.2f} us")
+        del cc
+
     ragged = None
     if args.ragged:
         ragged = ragged_round(x, wl, acc_in, page_table, stream, timed, n_part)
@@ -381,6 +402,7 @@ def main():
         "q_sweep": qsw,
         "verify_attention_cold": cold,
         "reference_copy": ref_copy,
+        "verify_attention_claimed": claimed,
         "ragged_round": ragged,
         "rejection_accept": stoch,
         "topk_candidates": topk,

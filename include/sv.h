@@ -54,6 +54,11 @@ typedef enum { SV_KV_FP16 = 0, SV_KV_FP8_E4M3 = 1 } sv_kv_dtype;
                                            workspace were not zero at the call: the result is wrong
                                            (they are zero again afterwards) */
 
+/* Bits of sv_verify_params.options. */
+#define SV_VERIFY_CLAIMED_WORK 0x1 /* opt-in run-time balancing of one long request (see
+                                      sv_verify_attention); results are then reproducible
+                                      to rounding only, and status_flags must be non-NULL */
+
 /*
  * Shape and layout of one verify call (host struct).
  *
@@ -93,16 +98,18 @@ typedef struct {
   int32_t num_splits;        /* 0 = automatic; > 0 forces the number of key chunks */
   int32_t window;            /* 0 = full attention; > 0: a sliding window of this many positions */
   int32_t sink;              /* with a window: leading positions every row also sees (0 = none) */
+  int32_t options;           /* SV_VERIFY_* bits; 0 = the default, bit-reproducible plan */
 } sv_verify_params;
 
 /*
  * Bytes of workspace sv_verify_attention needs for these parameters (0 when
  * one key chunk covers max_kv_len). Depends only on the host fields. Its
- * first 32 KB hold work counters and must be zero before the workspace's
- * first use, e.g. filled with zeros once when it is allocated: every verify
- * call leaves them zero again, so a workspace serves any number of verify
- * calls (also of other shapes), one at a time, but should not be shared with
- * other entry points' scratch. The partials follow.
+ * first 32 KB hold the work counters of the SV_VERIFY_CLAIMED_WORK option
+ * and must be zero before the workspace's first use with that option, e.g.
+ * filled with zeros once when it is allocated: every verify call leaves them
+ * zero again, so a workspace serves any number of verify calls (also of other
+ * shapes), one at a time, but should not be shared with other entry points'
+ * scratch. The default plan never reads them. The partials follow.
  */
 size_t sv_verify_workspace_bytes(const sv_verify_params* p);
 
@@ -141,13 +148,21 @@ sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t
  *
  * Arithmetic: fp16 (or exactly dequantised E4M3) inputs, fp32 accumulation;
  * the result does not depend on the number of splits beyond rounding.
- * Repeated calls give the same bits, except with fp16 keys, full attention,
- * q_len*Hq/Hkv <= 48, a split count that is a multiple of 8, at most 128
- * (request, KV head) groups and max_kv_len >= 4096 * splits (at least 64 key
- * steps of 16 per wave; e.g. 256K tokens at the automatic 64 splits of one
- * request, 32K at the 8 splits of 8 requests): there the waves of each group
- * claim 64-key grains at run time, so the order of the softmax updates, and
- * with it the rounding, varies between calls.
+ * Deterministic: every key chunk and the order of its softmax updates are
+ * fixed by the host fields and the device lengths, so repeated calls give the
+ * same bits, and so do calls whose physical pages are permuted (with the page
+ * table permuted alike).
+ *
+ * One exception, only on request (p->options & SV_VERIFY_CLAIMED_WORK): for
+ * one request (batch 1) with fp16 keys, full attention, q_len*Hq/Hkv <= 48, a
+ * split count that is a multiple of 8 and max_kv_len >= 4096 * splits (at
+ * least 64 key steps of 16 per wave, e.g. 256K tokens at the automatic 64
+ * splits), the waves of each KV head claim 64-key grains at run time, which
+ * evens out compute units that stream at different rates; the order of the
+ * softmax updates, and with it the rounding, then varies between calls.
+ * That mode needs status_flags (SV_ERR_INVALID_ARGUMENT otherwise), since a
+ * workspace whose counters are not zero is reported only there
+ * (SV_FLAG_WORKSPACE_NOT_ZERO). Elsewhere the option is ignored.
  */
 sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const void* k_pages,
                               const void* v_pages, const void* k_scales, const void* v_scales,

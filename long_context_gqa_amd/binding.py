@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libsv.so")
 SV_OK, SV_ERR_INVALID_ARGUMENT, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_HIP = range(5)
 SV_KV_FP16, SV_KV_FP8_E4M3 = 0, 1
 SV_FLAG_KV_LEN_ABOVE_BOUND, SV_FLAG_KV_LEN_BELOW_BLOCK, SV_FLAG_PAGE_ID_OUT_OF_RANGE = 1, 2, 4
-SV_FLAG_BAD_BLOCK_WIDTH = 8
+SV_FLAG_BAD_BLOCK_WIDTH, SV_FLAG_WORKSPACE_NOT_ZERO = 8, 0x10
+SV_VERIFY_CLAIMED_WORK = 0x1
 
 EXPORTED = (
     "sv_verify_workspace_bytes", "sv_verify_plan", "sv_verify_attention", "sv_verify_merge",
@@ -53,6 +54,7 @@ class SvVerifyParams(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("sink", ctypes.c_int32),
+        ("options", ctypes.c_int32),
     ]
 
 
@@ -136,11 +138,11 @@ def _check(status: int):
 
 def make_params(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                 max_pages_per_req, max_kv_len, kv_dtype=SV_KV_FP16, sm_scale=None, num_splits=0, window=0,
-                sink=0):
+                sink=0, options=0):
     if sm_scale is None:
         sm_scale = head_dim ** -0.5
     return SvVerifyParams(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                          max_pages_per_req, max_kv_len, kv_dtype, sm_scale, num_splits, window, sink)
+                          max_pages_per_req, max_kv_len, kv_dtype, sm_scale, num_splits, window, sink, options)
 
 
 def sv_verify_workspace_bytes(p: SvVerifyParams) -> int:
@@ -263,14 +265,16 @@ class VerifyCall:
     across launches (the benchmark times ``run`` in a loop)."""
 
     def __init__(self, q, k_pages, v_pages, page_table, kv_lens, q_len, max_kv_len,
-                 k_scales=None, v_scales=None, sm_scale=None, num_splits=0, with_lse=True, window=0, sink=0):
+                 k_scales=None, v_scales=None, sm_scale=None, num_splits=0, with_lse=True, window=0, sink=0,
+                 claim=False):
         dev = q.device
         B = kv_lens.shape[0]
         Hq, D = q.shape[1], q.shape[2]
         Hkv, P = k_pages.shape[1], k_pages.shape[2]
         dtype = SV_KV_FP8_E4M3 if k_pages.dtype == torch.uint8 else SV_KV_FP16
         self.params = make_params(B, q_len, Hq, Hkv, D, P, k_pages.shape[0], page_table.shape[1],
-                                  max_kv_len, dtype, sm_scale, num_splits, window, sink)
+                                  max_kv_len, dtype, sm_scale, num_splits, window, sink,
+                                  SV_VERIFY_CLAIMED_WORK if claim else 0)
         self.inputs = (q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens)
         self.out = torch.empty_like(q)
         self.out_lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=dev) if with_lse else None
@@ -287,12 +291,12 @@ class VerifyCall:
 
 
 def verify_attention(q, k_pages, v_pages, page_table, kv_lens, q_len, max_kv_len=None, k_scales=None,
-                     v_scales=None, sm_scale=None, num_splits=0, window=0, sink=0):
+                     v_scales=None, sm_scale=None, num_splits=0, window=0, sink=0, claim=False):
     """One verify-attention call; returns (out fp16, lse fp32, status flags)."""
     if max_kv_len is None:
         raise ValueError("max_kv_len (a host upper bound) is required")
     c = VerifyCall(q, k_pages, v_pages, page_table, kv_lens, q_len, max_kv_len, k_scales, v_scales, sm_scale,
-                   num_splits, window=window, sink=sink)
+                   num_splits, window=window, sink=sink, claim=claim)
     c.run()
     return c.out, c.out_lse, c.flags
 

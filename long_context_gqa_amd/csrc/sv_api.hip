@@ -62,8 +62,9 @@ struct Plan {
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
 
-// The first 256 bytes of a split workspace hold the claimed-work counters
-// (one int32 per KV head); the partials follow.
+// The first 32 KB of a split workspace hold the claimed-work counters (up to
+// 128 counters, each on its own 256-byte line; up to 16 per (request, KV
+// head) group); the partials follow.
 constexpr size_t kCounterBytes = sv::kCounterSlots * sv::kCounterStride * 4;
 
 constexpr int kMinChunk = 128;         // tokens; below this the partial traffic dominates
@@ -105,6 +106,8 @@ sv_status validate(const sv_verify_params* p) {
     return fail(SV_ERR_INVALID_ARGUMENT, "sink positions need a window (window 0 is full attention)");
   if (p->batch > 65535 || p->num_kv_heads > 65535)
     return fail(SV_ERR_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
+  if (p->options & ~SV_VERIFY_CLAIMED_WORK)
+    return fail(SV_ERR_INVALID_ARGUMENT, "unknown options bits 0x%x", (unsigned)p->options);
   return ok();
 }
 
@@ -162,7 +165,8 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   S = (maxkv + chunk - 1) / chunk;
   if (S * p->num_kv_heads * p->batch * 2 * rgs > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "too many workgroups (%lld splits)", S);
-  // One long request with fp16 keys, full attention and one row tile: the
+  // On request only (the rounding then varies between calls): one long
+  // request with fp16 keys, full attention and one row tile, whose
   // workgroups of each KV head (S a multiple of 8, so every head has
   // workgroups on all 8 XCDs) claim its keys in grains, which evens out XCDs
   // that stream at different rates. Only where every wave has about 64 steps
@@ -170,8 +174,8 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   // (only the device knows), and there the longest-first order of fixed
   // chunks beats an equal number of workgroups per request.
   pl->claim = false;
-  if (p->batch == 1 && p->window == 0 && p->kv_dtype == SV_KV_FP16 && pl->row_blocks == 1 &&
-      p->num_kv_heads <= sv::kCounterSlots) {
+  if ((p->options & SV_VERIFY_CLAIMED_WORK) && p->batch == 1 && p->window == 0 && p->kv_dtype == SV_KV_FP16 &&
+      pl->row_blocks == 1 && p->num_kv_heads <= sv::kCounterSlots) {
     const long long S8 = p->num_splits > 0 ? S : (S + 7) / 8 * 8;
     if (S8 >= 8 && S8 % 8 == 0 && (maxkv + 15) / 16 >= 64LL * sv::kWavesPerGroup * S8) {
       S = S8;
@@ -254,6 +258,9 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.part_o = pl.ws_bytes ? reinterpret_cast<float*>(ws + kCounterBytes) : nullptr;
   a.part_lse = pl.ws_bytes ? reinterpret_cast<float*>(ws + kCounterBytes + pl.part_o_bytes) : nullptr;
   const bool claim = pl.claim && !q_start;
+  // a dirty counter block is reported only through the flag word
+  if (claim && !status_flags)
+    return fail(SV_ERR_INVALID_ARGUMENT, "SV_VERIFY_CLAIMED_WORK needs a status_flags word");
   a.counters = claim ? reinterpret_cast<int32_t*>(ws) : nullptr;
   a.flags = status_flags;
   a.batch = p->batch;

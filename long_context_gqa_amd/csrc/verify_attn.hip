@@ -806,7 +806,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const int n_ctr = claim_counters(a.num_splits, a.batch * a.num_kv_heads);
   const int cidx = (ts + NTS * (split >> 3)) % n_ctr;
   int32_t* const ctr = CLAIM ? a.counters + ((b * a.num_kv_heads + g) * n_ctr + cidx) * kCounterStride : nullptr;
-  // pool grain of ticket t of this wave's counter (valid below c_ngr)
+  // pool grain of ticket t of this wave's counter (for valid tickets only:
+  // see `mine` below, which bounds t before the product is formed)
   auto grain_of = [&](int t) { return cidx + t * n_ctr; };
   int first_ticket = -1;
   if constexpr (CLAIM) {
@@ -855,8 +856,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // Claimed work: this wave's first segment (the static one, or a first
   // grain when the cache is too short for one) and the ticket of the next.
   int c_f = 0, c_pool0 = 0, c_ngr = 0, seg_base = 0, seg_nb = 0, ticket1 = -1;
+  // the grains this wave's counter deals: tickets 0 .. n_mine-1 are valid.
+  // Comparing the ticket itself keeps a counter that did not start at zero
+  // (any value) from forming an overflowing grain index.
+  int n_mine = 0;
+  auto mine = [&](int t) { return t >= 0 && t < n_mine; };
   if constexpr (CLAIM) {
     claim_layout(total, a.num_splits, &c_f, &c_pool0, &c_ngr);
+    n_mine = counter_grains(c_ngr, cidx, n_ctr);
     auto claim = [&]() {
       int t = 0;
       if (lane == 0) t = atomicAdd(ctr, 1);
@@ -868,7 +875,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       ticket1 = first_ticket;
     } else {
       const int t0c = first_ticket;
-      if (t0c >= 0 && grain_of(t0c) < c_ngr) {  // (a counter that did not start at 0 can give anything)
+      if (mine(t0c)) {  // (a counter that did not start at 0 can give anything)
         seg_base = c_pool0 + grain_of(t0c) * kGrain;
         seg_nb = min(kGrain, total - seg_base);
         ticket1 = claim();
@@ -1048,7 +1055,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       int base = seg_base, nb = my_steps, kk = 0;
       uint32_t rows = rows_first;
       int nbase = 0, nnb = 0;  // the successor (nnb 0: none)
-      if (ticket1 >= 0 && grain_of(ticket1) < c_ngr) {
+      if (mine(ticket1)) {
         nbase = c_pool0 + grain_of(ticket1) * kGrain;
         nnb = min(kGrain, total - nbase);
       }
@@ -1125,7 +1132,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
             nb = nnb;
             rows = nrows;
             kk = 0;
-            if (tnext >= 0 && grain_of(tnext) < c_ngr) {
+            if (mine(tnext)) {
               nbase = c_pool0 + grain_of(tnext) * kGrain;
               nnb = min(kGrain, total - nbase);
             } else {

@@ -259,9 +259,8 @@ def make_verify_inputs(wl: Workload, variant: str = "literal", device="cpu",
         k_scales = torch.empty((num_pages, Hkv, P, D // 64), dtype=torch.float16, device=device)
         v_scales = torch.empty_like(k_scales)
         _fill_fp8(kp, k_scales, wl.seed, S_K, dev_type, chunk_pages)
+        # (FP8 K/V are quantised from N(0,1) in both variants)
         _fill_fp8(vp, v_scales, wl.seed, S_V, dev_type, chunk_pages)
-        if variant == "literal":
-            pass  # FP8 K/V are quantised from N(0,1) in both variants
     else:
         raise ValueError(wl.kv_dtype)
 

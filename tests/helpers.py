@@ -33,13 +33,13 @@ def case(batch=1, q_len=8, lens=(100,), page_size=16, variant="unit", seed=7, or
     return W.make_verify_inputs(wl, variant, device=device, kv_lens=kv, spare_pages=spare)
 
 
-def run_gpu(x: W.VerifyInputs, num_splits=0, max_kv_len=None, kv_lens=None, page_table=None):
+def run_gpu(x: W.VerifyInputs, num_splits=0, max_kv_len=None, kv_lens=None, page_table=None, claim=False):
     dev = x.q.device
     kvl = (kv_lens if kv_lens is not None else x.kv_lens).to(dev)
     pt = (page_table if page_table is not None else x.page_table).to(dev).contiguous()
     mk = max_kv_len if max_kv_len is not None else int(kvl.max())
     out, lse, flags = B.verify_attention(x.q, x.k_pages, x.v_pages, pt, kvl, x.wl.q_len, mk,
-                                         x.k_scales, x.v_scales, x.sm_scale, num_splits)
+                                         x.k_scales, x.v_scales, x.sm_scale, num_splits, claim=claim)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), int(flags.item())
 
@@ -73,7 +73,17 @@ def check(out, lse, ref, ref_lse, mask=None, atol=ATOL, rtol_of_max=RTOL_OF_MAX,
     err = np.abs(o - r).max() if o.size else 0.0
     scale = np.abs(r).max() if r.size else 1.0
     lerr = np.abs(lse[mask] - ref_lse[mask]).max() if o.size else 0.0
-    say(f"  {what}: max|err| {err:.3e}  max|ref| {scale:.3e}  rel {err / max(scale, 1e-30):.3e}  lse err {lerr:.3e}")
+    # the same error in units of the output's own precision: distance to the
+    # fp16 rounding of the reference in fp16 ulps (0 or 1 for an exact
+    # kernel), and how far the error goes past that rounding's half ulp
+    ulps, past = 0.0, 0.0
+    if o.size:
+        r16 = r.astype(np.float16)
+        ulp = np.spacing(np.abs(r16)).astype(np.float64)
+        ulps = float((np.abs(o.astype(np.float64) - r16.astype(np.float64)) / ulp).max())
+        past = float(np.maximum(np.abs(o - r) - 0.5 * ulp, 0.0).max())
+    say(f"  {what}: max|err| {err:.3e}  max|ref| {scale:.3e}  rel {err / max(scale, 1e-30):.3e}  lse err {lerr:.3e}"
+        f"  fp16 ulps vs fp16(ref) {ulps:.0f}  beyond half an ulp {past:.2e}")
     assert err <= atol, f"{what}: max|err| {err} > {atol}"
     assert err <= rtol_of_max * scale, f"{what}: max|err| {err} > {rtol_of_max} * max|ref| {scale}"
     assert lerr <= LSE_ATOL, f"{what}: lse err {lerr}"

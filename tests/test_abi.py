@@ -229,3 +229,22 @@ def test_window_parameters_are_validated():
         B.sv_verify_plan(_p(sink=4))  # a sink without a window
     assert e.value.status == B.SV_ERR_INVALID_ARGUMENT
     assert B.sv_verify_plan(_p(window=2048, sink=4))[0] >= 1
+
+
+def test_options_are_validated_and_claimed_work_needs_a_flag_word():
+    # unknown option bits are refused on the host
+    with pytest.raises(B.SvError) as e:
+        B.sv_verify_plan(_p(options=0x2))
+    assert e.value.status == B.SV_ERR_INVALID_ARGUMENT
+    # one 512K request: the default plan and the claimed-work option both
+    # plan 64 splits; with the option the call needs a status_flags word
+    # (a dirty counter block is reported only there) and is refused first
+    kw = dict(max_kv_len=524296, max_pages_per_req=32769, num_pages=32769)
+    assert B.sv_verify_plan(_p(**kw)) == B.sv_verify_plan(_p(options=B.SV_VERIFY_CLAIMED_WORK, **kw))
+    lib = B.lib()
+    fake = 1 << 40
+    p = _p(options=B.SV_VERIFY_CLAIMED_WORK, **kw)
+    need = B.sv_verify_workspace_bytes(p)
+    st = lib.sv_verify_attention(ctypes.byref(p), fake, fake, fake, None, None, fake, fake, fake, None,
+                                 fake, need, None, None)
+    assert st == B.SV_ERR_INVALID_ARGUMENT and b"status_flags" in lib.sv_last_error()

@@ -1,5 +1,6 @@
-"""GPU parity of claimed work against the float64 oracle: requests with fp16
-keys whose split workgroups claim the keys in grains at run time (split
+"""GPU parity of claimed work (the SV_VERIFY_CLAIMED_WORK option) against the
+float64 oracle: requests with fp16 keys whose split workgroups claim the keys
+in grains at run time (split
 count a multiple of 8, at least 64 key steps per wave). Covered: forced 8
 and 16 splits over a 40K cache (static first segments, then grains, a last
 grain that ends inside a page), the same plan over much shorter actual
@@ -26,9 +27,9 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def plan(x, splits, max_kv):
+def plan(x, splits, max_kv, claim=True):
     c = B.VerifyCall(x.q, x.k_pages, x.v_pages, x.page_table.cuda().contiguous(), x.kv_lens.cuda(), x.wl.q_len,
-                     max_kv, x.k_scales, x.v_scales, x.sm_scale, splits)
+                     max_kv, x.k_scales, x.v_scales, x.sm_scale, splits, claim=claim)
     return c
 
 
@@ -39,7 +40,7 @@ def test_claimed_work_matches_oracle(q_len, splits, variant):
     c = plan(x, splits, KV)
     say(f"q={q_len} splits={splits} {variant}: plan {c.splits} x {c.chunk}")
     assert c.splits == splits
-    out, lse, flags = run_gpu(x, num_splits=splits)
+    out, lse, flags = run_gpu(x, num_splits=splits, claim=True)
     assert flags == 0
     ref, ref_lse = oracle(x)
     check(out, lse, ref, ref_lse, what=f"claimed q={q_len} S={splits}")
@@ -59,7 +60,7 @@ def test_claimed_work_over_shorter_actual_lengths(kv):
     # of the 32 waves per KV head get a grain
     x = case(1, 8, [KV], 16, "unit", seed=9)
     kvl = torch.tensor([kv], dtype=torch.int32)
-    out, lse, flags = run_gpu(x, num_splits=8, max_kv_len=KV, kv_lens=kvl)
+    out, lse, flags = run_gpu(x, num_splits=8, max_kv_len=KV, kv_lens=kvl, claim=True)
     assert flags == 0
     h = host(x)
     h["kv_lens"] = kvl
@@ -86,18 +87,27 @@ def test_counters_left_zero_and_a_dirty_workspace_is_flagged():
     # repeated calls agree to rounding (the grains' order varies)
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2e-3
-    # a workspace whose counters are not zero: flagged, and cleared again
-    c.workspace[:4].fill_(3)
-    c.flags.zero_()
-    c.run()
-    torch.cuda.synchronize()
-    assert int(c.flags.item()) & 0x10
-    assert int(c.workspace[:32768].count_nonzero().item()) == 0
-    c.flags.zero_()
-    c.run()
-    torch.cuda.synchronize()
-    assert int(c.flags.item()) == 0
-    check(c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask, what="after the reset")
+    # a workspace whose counters are not zero: flagged, and cleared again.
+    # Small, large (a leftover 1.0f, INT32_MAX) and negative values: a wave
+    # takes a ticket only below its counter's grain count, so none of them
+    # forms a grain index outside the cache
+    ctr = c.workspace[:32768].view(torch.int32)
+    for dirty in (3, 0x03030303, 0x3F800000, 0x7FFFFFFF, -5, -(1 << 31)):
+        ctr[0] = dirty
+        ctr[5 * 64] = dirty  # the counter on the sixth 256-byte line
+        c.flags.zero_()
+        c.run()
+        torch.cuda.synchronize()
+        say(f"  dirty counter {dirty}: flags {int(c.flags.item())}")
+        assert int(c.flags.item()) & 0x10
+        assert int(c.workspace[:32768].count_nonzero().item()) == 0
+        assert torch.isfinite(c.out.float()).all()
+        c.flags.zero_()
+        c.run()
+        torch.cuda.synchronize()
+        assert int(c.flags.item()) == 0
+        check(c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask,
+              what=f"after the reset ({dirty})")
 
 
 @pytest.mark.parametrize("lens,splits", [([KV] * 3, 8), ([KV, 9000, 300, KV - 20, 17], 8), ([70000, 70000], 16)])
@@ -108,7 +118,7 @@ def test_batches_keep_the_static_order(lens, splits):
     x = case(len(lens), 8, lens, 16, "unit", seed=len(lens) + splits)
     c = plan(x, splits, max(lens))
     say(f"batch {len(lens)} lens {lens} splits {splits}: plan {c.splits} x {c.chunk}")
-    out, lse, flags = run_gpu(x, num_splits=splits)
+    out, lse, flags = run_gpu(x, num_splits=splits, claim=True)
     assert flags == 0
     c.run()
     torch.cuda.synchronize()
@@ -129,7 +139,7 @@ def test_claimed_work_pages_and_heads(page, q_len, Hq, Hkv):
     x = case(1, q_len, [KV], page, "unit", seed=page + q_len + Hkv, Hq=Hq, Hkv=Hkv)
     c = plan(x, 8, KV)
     say(f"P={page} q={q_len} Hq={Hq} Hkv={Hkv}: plan {c.splits} x {c.chunk}")
-    out, lse, flags = run_gpu(x, num_splits=8)
+    out, lse, flags = run_gpu(x, num_splits=8, claim=True)
     assert flags == 0
     groups = [(0, 0), (0, Hkv - 1)]
     ref, ref_lse = oracle(x, groups=groups)
@@ -163,5 +173,5 @@ def test_claimed_work_replays_in_a_graph():
         assert int(c.flags.item()) == 0
         assert int(c.workspace[:32768].count_nonzero().item()) == 0
         check(c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask, what=f"replay {r}")
-        out2, lse2, flags2 = run_gpu(x, num_splits=8)  # eager work between replays
+        out2, lse2, flags2 = run_gpu(x, num_splits=8, claim=True)  # eager work between replays
         assert flags2 == 0

@@ -27,8 +27,10 @@ def _gpu():
                                      # 4,096 and more (row, head) items: one wave per item
                                      (7, 200, 24, 256), (20, 171, 24, 256), (3, 4096, 1, 100), (1, 512, 24, 256)])
 def test_merge_matches_oracle(S, R, H, D):
+    # order-one partials (each split's normalised output, N(0,1)); the merged
+    # row is a convex combination of them, so it is of order one as well
     g = torch.Generator().manual_seed(S * 7 + D)
-    po = torch.randn((S, R, H, D), generator=g) * 2
+    po = torch.randn((S, R, H, D), generator=g)
     pl = torch.randn((S, R, H), generator=g) * 3
     drop = torch.rand((S, R, H), generator=g) < 0.3
     pl[drop] = -float("inf")
@@ -42,8 +44,14 @@ def test_merge_matches_oracle(S, R, H, D):
     torch.cuda.synchronize()
     o, l = out.float().cpu().numpy(), lse.cpu().numpy()
     err = np.abs(o - ref).max()
-    say(f"S={S} R={R} H={H} D={D}: max|err| {err:.2e}")
-    assert err <= 2e-3 * max(1.0, np.abs(ref).max())
+    # the merge's own error: the fp16 rounding of the result (half an ulp of
+    # the reference's fp16 value) plus fp32 rounding in the weights and sums
+    ulp = np.spacing(np.abs(ref.astype(np.float16))).astype(np.float64)
+    past = (np.abs(o - ref) - 0.5 * ulp - 1e-5 * np.abs(po.numpy()).max()).max()
+    say(f"S={S} R={R} H={H} D={D}: max|err| {err:.2e}  max|ref| {np.abs(ref).max():.2f}  "
+        f"beyond half an ulp + fp32 bound {past:.2e}")
+    assert err <= 2e-3
+    assert past <= 0
     fin = np.isfinite(ref_lse)
     assert np.array_equal(fin, np.isfinite(l))
     if fin.any():
