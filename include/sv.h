@@ -51,8 +51,9 @@ typedef enum { SV_KV_FP16 = 0, SV_KV_FP8_E4M3 = 1 } sv_kv_dtype;
 #define SV_FLAG_BAD_BLOCK_WIDTH 0x8 /* a width outside 0..max, or packed rows outside 0..batch*max;
                                        that request is treated as having no block */
 #define SV_FLAG_WORKSPACE_NOT_ZERO 0x10 /* the work counters in the first 32 KB of the verify
-                                           workspace were not zero at the call: the result is wrong
-                                           (they are zero again afterwards) */
+                                           workspace were not zero at a call with
+                                           SV_VERIFY_CLAIMED_WORK: the result is wrong (they are
+                                           zero again afterwards) */
 
 /* Bits of sv_verify_params.options. */
 #define SV_VERIFY_CLAIMED_WORK 0x1 /* opt-in run-time balancing of one long request (see
@@ -119,7 +120,13 @@ size_t sv_verify_workspace_bytes(const sv_verify_params* p);
  * chunk s covers cache positions [s*chunk, (s+1)*chunk). With a sliding
  * window the chunks instead tile the positions a block can see (its sink
  * positions, then its window, in 16-position steps), so the split count
- * follows sink + window + q_len rather than max_kv_len. Host only.
+ * follows sink + window + q_len rather than max_kv_len. One exception: for
+ * one long request (batch 1, full attention, q_len*Hq/Hkv <= 48, a split
+ * count that is a multiple of 8 and max_kv_len >= 4096 * splits) the chunks
+ * of each KV head are spread over the GPU's 8 XCDs and those that run on the
+ * faster even XCDs are a few percent longer; their bounds are 16-position
+ * steps fixed by the request's length, and `chunk` is then the nominal
+ * length. Host only.
  */
 sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t* chunk_tokens);
 
@@ -238,6 +245,8 @@ size_t sv_greedy_accept_workspace_bytes(int32_t batch, int32_t q_len, int32_t vo
  *   argmax_ids  NULL or [batch*q_len] int32 (written)
  *   kv_lens_in, kv_lens_out  both NULL, or both [batch] int32 (may alias)
  *   workspace   sv_greedy_accept_workspace_bytes() bytes, 256-byte aligned
+ * Two launches (the slice scan, then one workgroup per request that reduces
+ * the slices and walks the drafts); nothing is kept between calls.
  */
 sv_status sv_greedy_accept(const float* logits, const int32_t* draft_ids, int32_t batch,
                            int32_t q_len, int32_t vocab, int32_t* accept_len, int32_t* bonus_ids,

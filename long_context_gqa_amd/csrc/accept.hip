@@ -96,6 +96,8 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* _
 // (each row by a team of lanes), then one thread walks the drafts.
 __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(AcceptLaunch a) {
   __shared__ int am_s[kMaxAcceptRows];
+  __shared__ int dr_s[kMaxAcceptRows];
+  __shared__ int kv_s;
   __shared__ Best red[kThreads];
   const int b = blockIdx.x, tid = threadIdx.x;
   const float2* __restrict__ ws = a.ws;
@@ -121,6 +123,10 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(AcceptLaunch 
     }
     dp = a.block_ids + r0 + 1;
   }
+  // the drafts and the length go to LDS up front, beside the slice reads, so
+  // the walk below is no chain of dependent global loads
+  for (int j = tid; j < q_len - 1; j += kThreads) dr_s[j] = dp[j];
+  if (tid == kThreads - 1 && a.kv_lens_out) kv_s = a.kv_lens_in[b];
   // team of lanes per row: the largest power of two with q_len teams <= 256
   int team = kThreads;
   while (team > 1 && team * q_len > kThreads) team >>= 1;
@@ -149,10 +155,10 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(AcceptLaunch 
   }
   if (tid == 0) {
     int acc = 0;
-    while (acc < q_len - 1 && dp[acc] == am_s[acc]) ++acc;
+    while (acc < q_len - 1 && dr_s[acc] == am_s[acc]) ++acc;
     a.accept_len[b] = acc;
     a.bonus_ids[b] = am_s[acc];
-    if (a.kv_lens_out) a.kv_lens_out[b] = a.kv_lens_in[b] - q_len + 1 + acc;
+    if (a.kv_lens_out) a.kv_lens_out[b] = kv_s - q_len + 1 + acc;
   }
 }
 

@@ -45,7 +45,7 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 // or belongs to no request).
 __device__ __forceinline__ int item_splits(const MergeArgs& a, int row) {
   int S = a.num_splits;
-  if (a.counters) return S;  // claimed work: every workgroup wrote its slot
+  if (a.counters || a.balanced) return S;  // claimed work, balanced chunks: every workgroup wrote its slot
   if (a.kv_lens) {
     // merge launched by the verify entry point: a request covered by a single
     // chunk was written directly, and chunks past its length hold nothing
@@ -81,10 +81,13 @@ __device__ __forceinline__ int item_splits(const MergeArgs& a, int row) {
 }
 
 // Claimed work: each grain counter must have ended at the number of grains
-// it deals plus the number of waves that claim from it (each fails once);
-// anything else means it did not start at zero (bit 0x10). Either way it is
-// left at zero for the next call. Runs once, in block 0, after the attention
-// kernel has finished.
+// it deals plus the number of waves that claim from it (each fails once),
+// and each group's tally of grains taken (word 1 of its first counter's
+// line) at the group's grain count; anything else means a counter did not
+// start at zero (bit 0x10): one that started a little above zero skips its
+// first grains yet ends at the clean value, which only the tally shows.
+// Either way both are left at zero for the next call. Runs once, in block 0,
+// after the attention kernel has finished.
 __device__ __forceinline__ void settle_counters(const MergeArgs& a) {
   const int groups = a.batch * a.num_kv_heads;
   const int C = a.counters ? claim_counters(a.num_splits, groups) : 1;
@@ -98,8 +101,13 @@ __device__ __forceinline__ void settle_counters(const MergeArgs& a) {
   // fails once
   const int want = counter_grains(n_grains, c, C) + a.num_splits / 2 / C * 8;
   int32_t* const ctr = a.counters + threadIdx.x * kCounterStride;
-  if (*ctr != want && a.flags) atomicOr(a.flags, 0x10);
+  bool dirty = *ctr != want;
   *ctr = 0;
+  if (c == 0) {
+    dirty = dirty || ctr[1] != n_grains;
+    ctr[1] = 0;
+  }
+  if (dirty && a.flags) atomicOr(a.flags, 0x10);
 }
 
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {

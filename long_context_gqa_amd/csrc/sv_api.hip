@@ -59,6 +59,7 @@ struct Plan {
   int rb, row_blocks;  // row blocks of 16 per workgroup; workgroups per (chunk, KV head, request)
   int splits, chunk;   // key chunks and their length in tokens
   bool claim;          // the keys of each (request, KV head) are claimed in grains (splits = slots per group)
+  bool balanced;       // XCD-balanced static chunks (splits = slots per group, a multiple of 8)
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
 
@@ -182,6 +183,22 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
       pl->claim = true;
     }
   }
+  // The default for long caches with fp16 keys, full attention and one row
+  // tile, when every request's S workgroups per KV head fit on the GPU in one
+  // round (one long request, or a batch of at most 256 / (Hkv * S)): static
+  // chunks spread over the 8 XCDs, the ones on even XCDs longer
+  // (xcd_chunk_start), which recovers what claiming does without giving up
+  // reproducible bits. Each request's chunks follow its own length, so a
+  // ragged batch of this size still ends with its longest request's slots.
+  pl->balanced = false;
+  if (!pl->claim && p->window == 0 && pl->row_blocks == 1 && p->kv_dtype == SV_KV_FP16) {
+    const long long S8 = p->num_splits > 0 ? S : (S + 7) / 8 * 8;
+    if (S8 >= 8 && S8 % 8 == 0 && (maxkv + 15) / 16 >= 64LL * sv::kWavesPerGroup * S8 &&
+        (long long)p->batch * p->num_kv_heads * S8 <= cu_count()) {
+      S = S8;
+      pl->balanced = true;
+    }
+  }
   pl->splits = (int)S;
   pl->chunk = (int)chunk;
   if (S > 1) {
@@ -279,6 +296,7 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.units = pl.splits * p->num_kv_heads * p->batch;
   a.window = p->window;
   a.sink = p->sink;
+  a.balanced = (pl.balanced && !q_start) ? 1 : 0;
   sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, claim, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
@@ -305,6 +323,7 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
     m.counters = a.counters;
     m.num_kv_heads = p->num_kv_heads;
     m.flags = status_flags;
+    m.balanced = a.balanced;
     sv::launch_merge(m, s);
     st = check_launch("verify_merge");
     if (st != SV_OK) return st;
@@ -356,6 +375,7 @@ sv_status sv_verify_merge(const float* part_o, const float* part_lse, int32_t nu
   m.counters = nullptr;
   m.num_kv_heads = 0;
   m.flags = nullptr;
+  m.balanced = 0;
   m.batch = 0;
   m.window = 0;
   m.sink = 0;

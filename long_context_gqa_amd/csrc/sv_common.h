@@ -41,6 +41,7 @@ struct AttnArgs {
   int32_t window, sink;  // sliding window (0: full attention) and leading sink positions
   float scale_log2;  // sm_scale * log2(e)
   int32_t* counters;  // claimed work: the grain counters of every (request, KV head) group
+  int32_t balanced;   // XCD-balanced static chunks (see xcd_chunk_start)
 };
 
 struct MergeArgs {
@@ -58,6 +59,7 @@ struct MergeArgs {
   int32_t* counters;
   int32_t num_kv_heads;
   int32_t* flags;
+  int32_t balanced;  // every split slot holds a partial (XCD-balanced static chunks)
 };
 
 // Length of request b as the kernels use it: the stored value clamped to the
@@ -151,6 +153,20 @@ __device__ inline void claim_layout(int total, int splits, int* f, int* pool0, i
   *f = ff;
   *pool0 = waves * ff;
   *n_grains = total > *pool0 ? (total - *pool0 + kGrain - 1) / kGrain : 0;
+}
+
+// XCD-balanced static chunks for one long request. The S workgroups of each
+// (request, KV head) group are spread over the 8 XCDs (slot s of the group
+// runs on XCD s mod 8, as workgroup ids go round-robin over the XCDs), and
+// since odd XCDs stream their keys measurably slower than even ones, a slot
+// on an even XCD gets a longer chunk: slot weights 1 + w and 1 - w (w =
+// kXcdWeight / 1000), so slot s starts at step
+//     floor(total * (1000 s + kXcdWeight (s mod 2)) / (1000 S))   (S even).
+// The boundaries are integers fixed by the length alone: the result is the
+// same to the bit on every call.
+constexpr int kXcdWeight = 70;  // best of 0..130 in an interleaved sweep at 512K
+__host__ __device__ inline int xcd_chunk_start(int total, int s, int S) {
+  return (int)(((long long)total * (1000LL * s + kXcdWeight * (s & 1))) / (1000LL * S));
 }
 
 void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, bool claim, hipStream_t s);

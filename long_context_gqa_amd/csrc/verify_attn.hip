@@ -743,11 +743,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // evenly over the XCDs. For 2..64 requests ordered_unit takes the full
   // chunks in that order, then the last partial chunks, longest first.
   int split, g, b;
-  if constexpr (CLAIM) {
+  if (CLAIM || a.balanced) {
     // S (a multiple of 8) workgroups per (request, KV head) group: group
     // (unit / 8) mod (B * Hkv), so each group's workgroups sit on all 8 XCDs
-    // and the faster XCDs can claim more of its keys. `split` is the
-    // workgroup's partial slot.
+    // and the faster XCDs can claim more of its keys (or, with balanced
+    // static chunks, get longer ones). `split` is the workgroup's partial
+    // slot; its XCD is split mod 8.
     const int grp = unit >> 3, n_grp = a.batch * a.num_kv_heads;
     g = (grp % n_grp) % a.num_kv_heads;
     b = (grp % n_grp) / a.num_kv_heads;
@@ -827,10 +828,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   const int total = WIN ? live_steps(kv, L, W, S, &n_sink, &w0) : (kv > 0 ? (kv + kStep - 1) / kStep : 0);
   const int cs = a.chunk / kStep;
   const int n_chunks = total > 0 ? (total + cs - 1) / cs : 1;
-  if (!CLAIM && split >= n_chunks) return;  // whole group: nothing of this request here
-  const bool direct = !CLAIM && (n_chunks == 1);
-  const int k_base = split * cs;
-  const int n_steps = min(total - k_base, cs) > 0 ? min(total - k_base, cs) : 0;
+  // (every slot of a balanced plan writes its partial, an empty one too)
+  if (!CLAIM && !a.balanced && split >= n_chunks) return;  // whole group: nothing of this request here
+  const bool direct = !CLAIM && !a.balanced && (n_chunks == 1);
+  int k_base = split * cs;
+  int n_steps = min(total - k_base, cs) > 0 ? min(total - k_base, cs) : 0;
+  if (!CLAIM && a.balanced) {
+    k_base = xcd_chunk_start(total, split, a.num_splits);
+    n_steps = xcd_chunk_start(total, split + 1, a.num_splits) - k_base;
+  }
   auto live_t0 = [&](int j) {
     const int k = k_base + j;
     if constexpr (!WIN) return kStep * k;
@@ -861,6 +867,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // (any value) from forming an overflowing grain index.
   int n_mine = 0;
   auto mine = [&](int t) { return t >= 0 && t < n_mine; };
+  // grains this wave took from its counter: added to the group's tally at
+  // the end, which the merge checks against the grain count (a counter that
+  // started above zero skips grains yet ends at the clean value)
+  int n_claimed = 0;
   if constexpr (CLAIM) {
     claim_layout(total, a.num_splits, &c_f, &c_pool0, &c_ngr);
     n_mine = counter_grains(c_ngr, cidx, n_ctr);
@@ -879,6 +889,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         seg_base = c_pool0 + grain_of(t0c) * kGrain;
         seg_nb = min(kGrain, total - seg_base);
         ticket1 = claim();
+        ++n_claimed;
       }
     }
   }
@@ -1058,6 +1069,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       if (mine(ticket1)) {
         nbase = c_pool0 + grain_of(ticket1) * kGrain;
         nnb = min(kGrain, total - nbase);
+        ++n_claimed;
       }
       uint32_t nrows = 0;
       int tnext = -1;
@@ -1135,6 +1147,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
             if (mine(tnext)) {
               nbase = c_pool0 + grain_of(tnext) * kGrain;
               nnb = min(kGrain, total - nbase);
+              ++n_claimed;
             } else {
               nnb = 0;
             }
@@ -1146,6 +1159,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         step_pv<RB>(vf, pb, ws, lane, kStep * (base + kk), kv);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // the group's tally of grains taken (word 1 of its first counter's line)
+      if (lane == 0 && n_claimed > 0)
+        atomicAdd(a.counters + (b * a.num_kv_heads + g) * n_ctr * kCounterStride + 1, n_claimed);
     } else
     for (int bstart = 0; bstart < my_steps; bstart += kWave) {
       const uint32_t rows = bstart == 0 ? rows_first : step_rows(bstart);

@@ -91,14 +91,19 @@ def test_counters_left_zero_and_a_dirty_workspace_is_flagged():
     # Small, large (a leftover 1.0f, INT32_MAX) and negative values: a wave
     # takes a ticket only below its counter's grain count, so none of them
     # forms a grain index outside the cache
+    # A counter a little above zero skips its first grains yet ends at the
+    # clean value: the group's tally of grains taken (word 1) shows it; a
+    # dirty tally alone is caught too
     ctr = c.workspace[:32768].view(torch.int32)
-    for dirty in (3, 0x03030303, 0x3F800000, 0x7FFFFFFF, -5, -(1 << 31)):
-        ctr[0] = dirty
-        ctr[5 * 64] = dirty  # the counter on the sixth 256-byte line
+    cases = [(0, v) for v in (1, 3, 0x03030303, 0x3F800000, 0x7FFFFFFF, -5, -(1 << 31))] + [(1, 3), (1, -1)]
+    for word, dirty in cases:
+        ctr[word] = dirty
+        if word == 0:
+            ctr[5 * 64] = dirty  # the counter on the sixth 256-byte line
         c.flags.zero_()
         c.run()
         torch.cuda.synchronize()
-        say(f"  dirty counter {dirty}: flags {int(c.flags.item())}")
+        say(f"  dirty word {word} = {dirty}: flags {int(c.flags.item())}")
         assert int(c.flags.item()) & 0x10
         assert int(c.workspace[:32768].count_nonzero().item()) == 0
         assert torch.isfinite(c.out.float()).all()
@@ -107,14 +112,15 @@ def test_counters_left_zero_and_a_dirty_workspace_is_flagged():
         torch.cuda.synchronize()
         assert int(c.flags.item()) == 0
         check(c.out.float().cpu().numpy(), c.out_lse.cpu().numpy(), ref, ref_lse, mask=mask,
-              what=f"after the reset ({dirty})")
+              what=f"after the reset (word {word} = {dirty})")
 
 
 @pytest.mark.parametrize("lens,splits", [([KV] * 3, 8), ([KV, 9000, 300, KV - 20, 17], 8), ([70000, 70000], 16)])
 def test_batches_keep_the_static_order(lens, splits):
-    # several requests never claim (their lengths may be ragged): the same
-    # plans as above over batches are exact against the oracle and, in the
-    # static order, give the same bits on every call
+    # several requests never claim (their lengths may be ragged), even with
+    # the option: the same plans as above over batches take static chunks
+    # (XCD-balanced ones where the grid fits the GPU in one round), are
+    # exact against the oracle and give the same bits on every call
     x = case(len(lens), 8, lens, 16, "unit", seed=len(lens) + splits)
     c = plan(x, splits, max(lens))
     say(f"batch {len(lens)} lens {lens} splits {splits}: plan {c.splits} x {c.chunk}")
