@@ -178,6 +178,29 @@ sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const vo
                               int32_t* status_flags, void* stream);
 
 /*
+ * sv_verify_attention for callers that cannot allocate device memory or pass
+ * a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same operation and the same kernels, with the
+ * workspace in the library's own device scratch of sv_verify_scratch_bytes()
+ * bytes (32 MiB), which each GPU the library runs on holds until the process
+ * ends. No allocation, no host synchronisation.
+ *
+ * Arguments and results as for sv_verify_attention, minus the workspace.
+ * A plan whose workspace exceeds the scratch (sv_verify_workspace_bytes(p) >
+ * sv_verify_scratch_bytes(), e.g. very large batches of q_len 16) returns
+ * SV_ERR_WORKSPACE_TOO_SMALL without launching. Every call on a GPU shares
+ * that GPU's scratch: calls that may overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. The first call
+ * on a device looks the scratch's device address up (hipGetSymbolAddress)
+ * with that device current; SV_ERR_HIP if that fails.
+ */
+size_t sv_verify_scratch_bytes(void);
+sv_status sv_verify_attention_noalloc(const sv_verify_params* p, const void* q, const void* k_pages,
+                                      const void* v_pages, const void* k_scales, const void* v_scales,
+                                      const int32_t* page_table, const int32_t* kv_lens, void* out,
+                                      float* out_lse, int32_t* status_flags, void* stream);
+
+/*
  * Merge of split-KV partials into the final attention output (the merge
  * step of compact online-softmax partials, PocketLLM page, "Implemented
  * execution path"): for every (row, head)

@@ -28,7 +28,7 @@ EXPORTED = (
     "sv_greedy_accept_ragged", "sv_prepare_block", "sv_append_kv", "sv_append_kv_fp8",
     "sv_rejection_accept_workspace_bytes",
     "sv_rejection_accept", "sv_topk_candidates_workspace_bytes", "sv_topk_candidates", "sv_status_string",
-    "sv_last_error", "sv_version",
+    "sv_last_error", "sv_version", "sv_verify_scratch_bytes", "sv_verify_attention_noalloc",
 )
 
 
@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.sv_verify_plan.restype = ctypes.c_int
         L.sv_verify_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, f32p, vp, sz, vp, vp]
         L.sv_verify_attention.restype = ctypes.c_int
+        L.sv_verify_scratch_bytes.argtypes = []
+        L.sv_verify_scratch_bytes.restype = sz
+        L.sv_verify_attention_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, f32p, vp, vp]
+        L.sv_verify_attention_noalloc.restype = ctypes.c_int
         L.sv_verify_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
         L.sv_verify_merge.restype = ctypes.c_int
         L.sv_greedy_accept_workspace_bytes.argtypes = [i32, i32, i32]
@@ -162,6 +166,17 @@ def sv_verify_attention(p: SvVerifyParams, q, k_pages, v_pages, k_scales, v_scal
                                       _ptr(v_scales), _ptr(page_table), _ptr(kv_lens), _ptr(out),
                                       _ptr(out_lse), _ptr(workspace), ws_bytes, _ptr(status_flags),
                                       _stream(stream)))
+
+
+def sv_verify_scratch_bytes() -> int:
+    return int(lib().sv_verify_scratch_bytes())
+
+
+def sv_verify_attention_noalloc(p: SvVerifyParams, q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens,
+                                out, out_lse=None, status_flags=None, stream=None):
+    _check(lib().sv_verify_attention_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                             _ptr(k_scales), _ptr(v_scales), _ptr(page_table), _ptr(kv_lens),
+                                             _ptr(out), _ptr(out_lse), _ptr(status_flags), _stream(stream)))
 
 
 def sv_verify_merge(part_o, part_lse, out, out_lse=None, stream=None):

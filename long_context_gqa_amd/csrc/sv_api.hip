@@ -331,9 +331,62 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   return ok();
 }
 
+// Scratch of the allocation-free entry point: the workspace of one verify
+// call, in the library's own device memory (zero at load, which the
+// claimed-work counters at its start need; every call leaves them zero).
+// Each device that runs the library holds one copy until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call there (with that device current) and kept per device.
+sv_status scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SV_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SV_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    cache[dev] = p;
+  }
+  *ptr = cache[dev];
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t sv_verify_scratch_bytes(void) { return kScratchBytes; }
+
+sv_status sv_verify_attention_noalloc(const sv_verify_params* p, const void* q, const void* k_pages,
+                                      const void* v_pages, const void* k_scales, const void* v_scales,
+                                      const int32_t* page_table, const int32_t* kv_lens, void* out,
+                                      float* out_lse, int32_t* status_flags, void* stream) {
+  Plan pl;
+  sv_status st = make_plan(p, &pl);
+  if (st != SV_OK) return st;
+  if (pl.ws_bytes > kScratchBytes)
+    return fail(SV_ERR_WORKSPACE_TOO_SMALL,
+                "this plan needs %zu bytes of workspace; the library's scratch holds %zu "
+                "(use sv_verify_attention with a workspace)",
+                pl.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = scratch_address(&ws);
+    if (st != SV_OK) return st;
+  }
+  return verify_attention_impl(p, nullptr, q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens, out,
+                               out_lse, ws, pl.ws_bytes, status_flags, stream);
+}
 
 sv_status sv_verify_attention(const sv_verify_params* p, const void* q, const void* k_pages,
                               const void* v_pages, const void* k_scales, const void* v_scales,

@@ -248,3 +248,21 @@ def test_options_are_validated_and_claimed_work_needs_a_flag_word():
     st = lib.sv_verify_attention(ctypes.byref(p), fake, fake, fake, None, None, fake, fake, fake, None,
                                  fake, need, None, None)
     assert st == B.SV_ERR_INVALID_ARGUMENT and b"status_flags" in lib.sv_last_error()
+
+
+def test_noalloc_entry_point_refuses_plans_beyond_its_scratch():
+    # the ragged 32 x 131K q=16 workload's plan needs about 200 MB of
+    # workspace: more than the library's 32 MiB scratch, refused before any
+    # device call
+    lib = B.lib()
+    assert B.sv_verify_scratch_bytes() == 32 << 20
+    p = _p(batch=32, q_len=16, page_size=64, max_kv_len=131088, max_pages_per_req=2049, num_pages=65568)
+    assert B.sv_verify_workspace_bytes(p) > B.sv_verify_scratch_bytes()
+    fake = 1 << 40
+    st = lib.sv_verify_attention_noalloc(ctypes.byref(p), fake, fake, fake, None, None, fake, fake, fake, None,
+                                         None, None)
+    assert st == B.SV_ERR_WORKSPACE_TOO_SMALL and b"scratch" in lib.sv_last_error()
+    # bad shapes are refused as by sv_verify_attention
+    st = lib.sv_verify_attention_noalloc(ctypes.byref(_p(head_dim=128)), fake, fake, fake, None, None, fake, fake,
+                                         fake, None, None, None)
+    assert st == B.SV_ERR_UNSUPPORTED
