@@ -69,7 +69,10 @@ struct Plan {
 constexpr size_t kCounterBytes = sv::kCounterSlots * sv::kCounterStride * 4;
 
 constexpr int kMinChunk = 128;         // tokens; below this the partial traffic dominates
-constexpr int kBatchChunkCap = 8192;   // tokens; largest automatic chunk for a batch of requests
+// largest automatic chunk for a batch of requests: 8 MiB of K/V per (request,
+// KV head), i.e. 8,192 fp16 tokens or 16,384 FP8 tokens (528 B per token,
+// taken as half of fp16's 1,024)
+constexpr int kBatchChunkCap = 8192;
 constexpr int kGroupsPerCU = 1;        // workgroups per CU the automatic plan aims at (LDS and registers allow one)
 
 sv_status validate(const sv_verify_params* p) {
@@ -142,9 +145,10 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     const long long target = (long long)kGroupsPerCU * cu_count();
     S = (target + groups - 1) / groups;
     long long chunk = (maxkv + S - 1) / S;
-    if (p->batch > 1 && chunk > kBatchChunkCap) {
+    const long long cap = p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * kBatchChunkCap : kBatchChunkCap;
+    if (p->batch > 1 && chunk > cap) {
       // a whole multiple of the fill count keeps full rounds of workgroups
-      S *= chunk / kBatchChunkCap;
+      S *= chunk / cap;
       chunk = (maxkv + S - 1) / S;
     }
     if (chunk < kMinChunk) chunk = kMinChunk;

@@ -107,12 +107,17 @@ struct RowMask {
   int lim[RB];
   int lo[RB];
   int sink;
+  int lim_min;  // smallest lim over the wave's rows (wave-uniform)
+  int lo_max;   // largest lo over the wave's rows (wave-uniform)
 };
 
 // Masking of one step's scores (lane holds tokens t0 + 4*(lane/16) + i of row
 // lane%16 in each row block), without branches.
 template <int RB, bool WIN>
 __device__ __forceinline__ void apply_mask(float (&x)[RB][4], const RowMask<RB, WIN>& mk, int lane, int t0) {
+  // a step wholly below every row's limit (and, with a window, above every
+  // row's lower edge) needs no masking: a wave-uniform test
+  if (t0 + kStep <= mk.lim_min && (!WIN || t0 >= mk.lo_max)) return;
   const int tok = t0 + 4 * (lane >> 4);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -248,18 +253,6 @@ __device__ __forceinline__ void softmax_p(const float (&x)[RB][4], const WaveSta
 }
 
 template <int RB>
-__device__ __forceinline__ void softmax_pf(const float (&x)[RB][4], const WaveState<RB>& ws, float (&lsum)[RB],
-                                           float (&p)[RB][4]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float ref = (ws.m[rb] == -INFINITY) ? 0.f : ws.m[rb];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[rb][i] = exp2_fast(x[rb][i] - ref);
-    lsum[rb] = (p[rb][0] + p[rb][1]) + (p[rb][2] + p[rb][3]);
-  }
-}
-
-template <int RB>
 __device__ __forceinline__ void rescale_o(WaveState<RB>& ws, const float (&alpha)[RB]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -307,36 +300,53 @@ __device__ __forceinline__ float half_at(const u32x4 (&h)[2], int idx) {
 
 // O^T += V^T . P^T for one FP8 step: MFMA block j = 4*bb + c holds channels
 // 64*bb + 4*(lane%16) + c, all inside scale block bb, so the V scale is folded
-// into P^T once per block group and V is used exactly.
+// into P^T once per block group and V is used exactly. P^T arrives in fp16
+// (as for fp16 KV); each token pair's P is multiplied by its pair of V scales
+// with one packed fp16 multiply.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 template <int RB, bool MASK = true>
-__device__ __forceinline__ void step_pv8(VFrag8& vf, const u32x4 (&sv)[2], const float (&p)[RB][4],
+__device__ __forceinline__ void step_pv8(VFrag8& vf, const u32x4 (&sv)[2], const half4_t (&ph)[RB],
                                          WaveState<RB>& ws, int lane, int t0, int kv) {
   const int hi = lane >> 4;
-  float fv[4][4];  // [token i][block]
+  // V scales of tokens (0, 1) and (2, 3) of the lane's group, per block bb,
+  // as half pairs: the scale of token i, block bb is half 4i + bb of sv
+  // (dword 2i + bb/2, low half for even bb)
+  uint32_t s01[4], s23[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) fv[i][bb] = half_at(sv, 4 * i + bb);
+  for (int bb = 0; bb < 4; ++bb) {
+    const uint32_t sel = (bb & 1) ? 0x07060302u : 0x05040100u;
+    const int d = bb >> 1;
+    s01[bb] = __builtin_amdgcn_perm(sv[0][2 + d], sv[0][d], sel);
+    s23[bb] = __builtin_amdgcn_perm(sv[1][2 + d], sv[1][d], sel);
+  }
   // Keys at or past kv_len: weight 0; their (poison) scales must not enter
   // and their bytes may decode to NaN (0 * NaN is NaN), so clear both.
   if (MASK && t0 + kStep > kv) {
+    const int tok = t0 + 4 * hi;
+    const uint32_t m01 = (tok + 0 < kv ? 0x0000ffffu : 0u) | (tok + 1 < kv ? 0xffff0000u : 0u);
+    const uint32_t m23 = (tok + 2 < kv ? 0x0000ffffu : 0u) | (tok + 3 < kv ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      s01[bb] &= m01;
+      s23[bb] &= m23;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (t0 + 4 * hi + i >= kv) {
+      if (tok + i >= kv) {
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          fv[i][bb] = 0.f;
-          vf.v[4 * i + bb] = 0u;
-        }
+        for (int bb = 0; bb < 4; ++bb) vf.v[4 * i + bb] = 0u;
       }
   }
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
     half4_t pb[RB];
+    const half2_t a01 = __builtin_bit_cast(half2_t, s01[bb]), a23 = __builtin_bit_cast(half2_t, s23[bb]);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      pb[rb] = half4_t{(_Float16)(p[rb][0] * fv[0][bb]), (_Float16)(p[rb][1] * fv[1][bb]),
-                       (_Float16)(p[rb][2] * fv[2][bb]), (_Float16)(p[rb][3] * fv[3][bb])};
+    for (int rb = 0; rb < RB; ++rb) {
+      const half2_t q01 = half2_t{ph[rb][0], ph[rb][1]} * a01;
+      const half2_t q23 = half2_t{ph[rb][2], ph[rb][3]} * a23;
+      pb[rb] = half4_t{q01[0], q01[1], q23[0], q23[1]};
+    }
     // tokens (0, 1) and (2, 3) of the lane's group, byte c of block bb, as
     // fp16 pairs: A operand halves of channel 64*bb + 4*(lane%16) + c
     const uint32_t z01l = zip_lo(vf.v[bb], vf.v[4 + bb]), z01h = zip_hi(vf.v[bb], vf.v[4 + bb]);
@@ -596,7 +606,9 @@ __device__ __forceinline__ void ring_read_v8(VFrag8& f, uint32_t addr) {
 // The scaled scores of one FP8 step: per 64-channel block, two matrix ops
 // on the converted K and the wave's Q fragments (in registers), one
 // accumulator per (row block, scale block) so the block scales are applied
-// after all matrix ops are issued: S = sum_b scale_b * partial_b.
+// after all matrix ops are issued: S = sum_b scale_b * partial_b, one
+// multiply and three fused multiply-adds per score, the softmax scale applied
+// once at the end.
 template <int RB>
 __device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4 (&qa)[RB][8], float scale_log2,
                                              float (&x)[RB][4]) {
@@ -621,13 +633,17 @@ __device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4 (&qa)
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk) * scale_log2;
+    for (int bk = 0; bk < 4; ++bk) fk[i][bk] = half_at(kf.sk, 4 * i + bk);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[rb][i] = (fk[i][0] * acc[rb][0][i] + fk[i][1] * acc[rb][1][i]) +
-                 (fk[i][2] * acc[rb][2][i] + fk[i][3] * acc[rb][3][i]);
+    for (int i = 0; i < 4; ++i) {
+      float t = fk[i][0] * acc[rb][0][i];
+      t = __builtin_fmaf(fk[i][1], acc[rb][1][i], t);
+      t = __builtin_fmaf(fk[i][2], acc[rb][2][i], t);
+      t = __builtin_fmaf(fk[i][3], acc[rb][3][i], t);
+      x[rb][i] = t * scale_log2;
+    }
 }
 
 constexpr int kRingStage = 16384;  // K (8 KB) + V (8 KB) of one step
@@ -957,12 +973,23 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   // padding rows see every key
   RowMask<RB, WIN> mk;
   mk.sink = S;
+  int lmin = INT32_MAX, lmax = INT32_MIN;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = growbase + rb * 16 + (lane & 15);
     mk.lim[rb] = r < R ? min(L + r / G + 1, kv) : kv;
     mk.lo[rb] = r < R ? L + r / G + 1 - W : INT32_MIN;
+    lmin = min(lmin, mk.lim[rb]);
+    lmax = max(lmax, mk.lo[rb]);
   }
+  // across the wave (every lane takes part): the smallest limit, the largest lower edge
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lmin = min(lmin, __shfl_xor(lmin, o));
+    lmax = max(lmax, __shfl_xor(lmax, o));
+  }
+  mk.lim_min = __builtin_amdgcn_readfirstlane(lmin);
+  mk.lo_max = __builtin_amdgcn_readfirstlane(lmax);
   if constexpr (FP8) {
     // ---- FP8: each wave owns its token steps and a private one-step ring ----
     // (same schedule as the fp16 ring below; half-steps are K bytes + both
@@ -998,15 +1025,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       // Software pipeline as in the fp16 loop: step k's PV runs while step
       // k+1's softmax is computed (same read order, so the same waits).
       auto sbase = [&](int kk) { return ring_lds + (kk & (DEPTH - 1)) * kStage8; };
-      float pr[RB][4];
+      half4_t pr[RB];
       u32x4 sv[2];  // V scales of the step whose PV is next
       {
         KFrag8 kf;
         ring_read_k8<kWaitK>(kf, sbase(0) + k8_lane_off(lane), sbase(0) + 8192 + 32 * (lane >> 4));
         issue_k(min(DEPTH, nb - 1), 0);
-        float x0[RB][4];
+        float x0[RB][4], p0[RB][4];
         scores8_mfma<RB>(kf, qa, a.scale_log2, x0);
-        softmax_step<RB>(x0, ws, pr, lane, step_t0(0), mk);
+        softmax_step<RB>(x0, ws, p0, lane, step_t0(0), mk);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          pr[rb] = half4_t{(_Float16)p0[rb][0], (_Float16)p0[rb][1], (_Float16)p0[rb][2], (_Float16)p0[rb][3]};
         sv[0] = kf.sv[0];
         sv[1] = kf.sv[1];
       }
@@ -1025,12 +1055,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         sv[0] = kf.sv[0];
         sv[1] = kf.sv[1];
         const bool any = mask_check<RB>(x, lmx, ws, mk, lane, step_t0(kk + 1));
-        softmax_pf<RB>(x, ws, lsum, pr);
+        softmax_p<RB>(x, ws, lsum, pr);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) alpha[rb] = 1.f;
         if (any) {
           move_ref<RB>(lmx, ws, alpha);
-          softmax_pf<RB>(x, ws, lsum, pr);
+          softmax_p<RB>(x, ws, lsum, pr);
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) ws.l[rb] = ws.l[rb] * alpha[rb] + lsum[rb];
