@@ -266,3 +266,21 @@ def test_noalloc_entry_point_refuses_plans_beyond_its_scratch():
     st = lib.sv_verify_attention_noalloc(ctypes.byref(_p(head_dim=128)), fake, fake, fake, None, None, fake, fake,
                                          fake, None, None, None)
     assert st == B.SV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("batch,q_len,max_kv,page,dtype,splits", [
+    (1, 8, 4104, 16, B.SV_KV_FP16, 33),            # 4K: chunks of 128 (the smallest)
+    (8, 8, 32776, 16, B.SV_KV_FP16, 8),            # 8 x 32K: one round, XCD-balanced
+    (1, 8, 524296, 16, B.SV_KV_FP16, 64),          # 512K: one workgroup per CU, XCD-balanced
+    (32, 16, 131088, 64, B.SV_KV_FP16, 16),        # ragged q=16 bound: 8K-token chunk cap
+    (4, 8, 262152, 16, B.SV_KV_FP8_E4M3, 16),      # FP8 4 x 262K: 16K-token cap (8 MiB of K/V)
+])
+def test_plans_of_the_benchmark_workloads(batch, q_len, max_kv, page, dtype, splits):
+    # the planner's choices for the five workloads (256 compute units assumed
+    # when no GPU is present, as on the MI355X)
+    pages = -(-max_kv // page)
+    p = _p(batch=batch, q_len=q_len, page_size=page, max_kv_len=max_kv, max_pages_per_req=pages,
+           num_pages=pages * batch, kv_dtype=dtype)
+    s, c = B.sv_verify_plan(p)
+    assert s == splits, (s, c)
+    assert c % 64 == 0 and s * c >= max_kv
