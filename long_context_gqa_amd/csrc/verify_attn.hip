@@ -281,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   __syncthreads();
 
   WaveState<RB> ws;
+  ws.c = a.scale_log2;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     ws.m[rb] = -INFINITY;
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         ring_read_k8<kWaitK>(kf, sbase(0) + k8_lane_off(lane), sbase(0) + 8192 + 32 * (lane >> 4));
         issue_k(min(DEPTH, nb - 1), 0);
         float x0[RB][4], p0[RB][4];
-        scores8_mfma<RB>(kf, qa, a.scale_log2, x0);
+        scores8_mfma<RB>(kf, qa, x0);
         softmax_step<RB>(x0, ws, p0, lane, step_t0(0), mk);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         ring_read_k8<kWaitK>(kf, sbase(kk + 1) + k8_lane_off(lane), sbase(kk + 1) + 8192 + 32 * (lane >> 4));
         issue_k(min(kk + 1 + DEPTH, nb - 1), (kk + 1) & (DEPTH - 1));
         float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
-        scores8_mfma<RB>(kf, qa, a.scale_log2, x);
+        scores8_mfma<RB>(kf, qa, x);
         // (a step before the wave's last of the batch ends below kv_len)
         step_pv8<RB, false>(vf, sv, pr, ws, lane, t0, kv);
         sv[0] = kf.sv[0];
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
           KFrag kf;
           ring_read8<kWait, 64>(kf.k, ring_lds + k_lane_off(lane));
           dma_k<0, 8>(kpool + tgt(1) * kHeadDim, ring, lane);
-          step_scores<RB>(kf, qa, ws, pb, lane, kStep * base, mk, a.scale_log2);
+          step_scores<RB>(kf, qa, ws, pb, lane, kStep * base, mk);
         }
         for (;;) {
           if (kk + 1 >= nb && nnb == 0) break;  // step kk is the wave's last
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
             ring_read8_acc<kWait, 64>(kf.k, ring_lds + k_lane_off(lane));
           dma_k<0, 8>(kpool + tgt(kk + 2) * kHeadDim, ring, lane);
           float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
-          scores_mfma<RB>(kf, qa, a.scale_log2, x);
+          scores_mfma<RB>(kf, qa, x);
           // (only the stream's last step can end above kv_len)
           step_pv<RB, false>(vf, pb, ws, lane, t0, kv);
           const bool any = mask_check<RB, WIN, false>(x, lmx, ws, mk, lane, t1);
@@ -549,9 +550,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         KFrag kf;
         ring_read8<kWait, 64>(kf.k, ring_lds + stage(0) + k_lane_off(lane));
         dma_k<0, 8>(step_base(min(DEPTH, nb - 1), kpool), ring + stage(0), lane);
-        step_scores<RB>(kf, qa, ws, pb, lane, step_t0(0), mk, a.scale_log2);
+        step_scores<RB>(kf, qa, ws, pb, lane, step_t0(0), mk);
       }
-      for (int kk = 0; kk + 1 < nb; ++kk) {
+      auto body = [&](int kk, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         const int t0 = step_t0(kk);
         const int st = stage(kk), st1 = stage(kk + 1);
         VFrag vf;
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         ring_read8_acc<kWait, 64>(kf.k, ring_lds + st1 + k_lane_off(lane));
         dma_k<0, 8>(step_base(min(kk + 1 + DEPTH, nb - 1), kpool), ring + st1, lane);
         float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
-        scores_mfma<RB>(kf, qa, a.scale_log2, x);
+        scores_mfma<RB>(kf, qa, x);
         // (a step before the wave's last of the batch ends below kv_len)
         step_pv<RB, false>(vf, pb, ws, lane, t0, kv);
         // (masking without the skip test, and the softmax kept ahead of the
@@ -569,7 +571,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         // matrix ops, where the scheduler interleaves the two; the FP8 loop
         // above, whose vector work already fills that time, keeps the test,
         // which measured faster there)
-        const bool any = mask_check<RB, WIN, false>(x, lmx, ws, mk, lane, step_t0(kk + 1));
+        bool any;
+        if constexpr (MASKED) any = mask_check<RB, WIN, false>(x, lmx, ws, mk, lane, step_t0(kk + 1));
+        else any = max_check<RB>(x, lmx, ws);
         softmax_p<RB>(x, ws, lsum, pb);
         pin_softmax<RB>(pb, lsum);
 #pragma unroll
@@ -581,7 +585,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) ws.l[rb] = ws.l[rb] * alpha[rb] + lsum[rb];
         if (any) rescale_o<RB>(ws, alpha);
+      };
+      // Full attention: only the wave's last steps (the causal diagonal and
+      // the tail) can need masking; the iterations before them (whose next
+      // step ends at or below every row's limit) run without it.
+      int kk = 0, clean = 0;
+      if constexpr (!WIN) {
+        const int span = mk.lim_min - kStep - step_t0(1);
+        clean = span < 0 ? 0 : min(nb - 1, span / (kStep * NTS) + 1);
       }
+      for (; kk < clean; ++kk) body(kk, std::false_type{});
+      for (; kk + 1 < nb; ++kk) body(kk, std::true_type{});
       {
         VFrag vf;
         ring_read_vt<kWait>(vf, ring_lds + stage(nb - 1) + 8192 + v_lane_off(lane), lane);

@@ -68,6 +68,7 @@ struct WaveState {
   floatx4 o[RB][16];  // O^T accumulators: block j, rows of this lane
   float m[RB];        // reference (log2 units, >= every score seen - 8) of row lane%16
   float l[RB];        // this lane's share of the running sum
+  float c;            // sm_scale * log2(e): a raw score q.k times c is in log2 units
 };
 
 // The keys each of a lane's rows sees: t < lim (causal and tail limit) and,
@@ -104,8 +105,9 @@ __device__ __forceinline__ void apply_mask(float (&x)[RB][4], const RowMask<RB, 
     }
 }
 
-// Online-softmax update of one step from the scaled scores x (log2 units):
-// masking, the lazy reference, the running sum, and p.
+// Online-softmax update of one step from the raw scores x (q.k; x * c is in
+// log2 units): masking, the lazy reference, the running sum, and p. The max
+// is taken on raw scores (scaling by c > 0, rounded, keeps the order).
 template <int RB, bool WIN>
 __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& ws, float (&p)[RB][4],
                                              int lane, int t0, const RowMask<RB, WIN>& mk) {
@@ -115,11 +117,12 @@ __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& w
     float mx = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx *= ws.c;
     // Lazy reference: the row's reference m only moves when the tile max
-    // exceeds it by more than kLazyLog2, so p = 2^(x - m) <= 2^kLazyLog2 stays
-    // well inside fp16 and the O/l rescale (64*RB accumulators) is rare.
-    // Numerator and denominator share the reference, so the result is the
-    // same softmax.
+    // exceeds it by more than kLazyLog2, so p = 2^(x c - m) <= 2^kLazyLog2
+    // stays well inside fp16 and the O/l rescale (64*RB accumulators) is
+    // rare. Numerator and denominator share the reference, so the result is
+    // the same softmax.
     const bool bump = mx > ws.m[rb] + kLazyLog2;
     if (__any(bump)) {
       const float mnew = bump ? mx : ws.m[rb];
@@ -131,38 +134,33 @@ __device__ __forceinline__ void softmax_step(float (&x)[RB][4], WaveState<RB>& w
     }
     const float ref = (ws.m[rb] == -INFINITY) ? 0.f : ws.m[rb];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[rb][i] = exp2_fast(x[rb][i] - ref);
+    for (int i = 0; i < 4; ++i) p[rb][i] = exp2_fast(__builtin_fmaf(x[rb][i], ws.c, -ref));
     ws.l[rb] += (p[rb][0] + p[rb][1]) + (p[rb][2] + p[rb][3]);
   }
 }
 
-// The scaled scores of one fp16 step: per row block, the 8 k-steps of the
+// The raw scores of one fp16 step: per row block, the 8 k-steps of the
 // score matrix ops on the K fragments and the wave's Q fragments (held in
-// registers for the whole loop), in two independent chains.
+// registers for the whole loop), one accumulation chain per row block (the
+// row blocks' chains interleave).
 template <int RB>
-__device__ __forceinline__ void scores_mfma(const KFrag& kf, const u32x4 (&qa)[RB][8], float scale_log2,
-                                            float (&x)[RB][4]) {
+__device__ __forceinline__ void scores_mfma(const KFrag& kf, const u32x4 (&qa)[RB][8], float (&x)[RB][4]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; s += 2) {
-      a0 = mfma_16x16x32(kf.k[s], qa[rb][s], a0);
-      a1 = mfma_16x16x32(kf.k[s + 1], qa[rb][s + 1], a1);
-    }
-    const floatx4 acc = a0 + a1;
+    for (int s = 0; s < 8; ++s) acc = mfma_16x16x32(kf.k[s], qa[rb][s], acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[rb][i] = acc[i] * scale_log2;
+    for (int i = 0; i < 4; ++i) x[rb][i] = acc[i];
   }
 }
 
 // Scores of one fp16 step and the fp16 P^T fragments.
 template <int RB, bool WIN>
 __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4 (&qa)[RB][8], WaveState<RB>& ws,
-                                            half4_t (&pb)[RB], int lane, int t0, const RowMask<RB, WIN>& mk,
-                                            float scale_log2) {
+                                            half4_t (&pb)[RB], int lane, int t0, const RowMask<RB, WIN>& mk) {
   float x[RB][4];
-  scores_mfma<RB>(kf, qa, scale_log2, x);
+  scores_mfma<RB>(kf, qa, x);
   float p[RB][4];
   softmax_step<RB>(x, ws, p, lane, t0, mk);
 #pragma unroll
@@ -173,7 +171,7 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4 (&qa)[R
 // The pieces of one step for the software-pipelined fp16 loop, where the PV
 // matrix ops of step k are issued right after the score matrix ops of step
 // k+1, and the softmax of k+1 fills their shadow:
-//   scores_mfma   the scaled scores of step k+1 (Q fragments in registers);
+//   scores_mfma   the raw scores of step k+1 (Q fragments in registers);
 //   mask_check    causal/tail masking without branches (per-row limits are
 //                 computed once), each lane's own max, and whether any lane
 //                 needs its row's reference moved;
@@ -184,17 +182,22 @@ __device__ __forceinline__ void step_scores(const KFrag& kf, const u32x4 (&qa)[R
 //                 matrix ops; redone after a move);
 //   rescale_o     (rare) O *= alpha, after step k's PV was accumulated at the
 //                 old reference.
-template <int RB, bool WIN, bool SKIP = true>
-__device__ __forceinline__ bool mask_check(float (&x)[RB][4], float (&lmx)[RB], const WaveState<RB>& ws,
-                                           const RowMask<RB, WIN>& mk, int lane, int t0) {
-  apply_mask<RB, WIN, SKIP>(x, mk, lane, t0);
+// (max_check: the same for a step that needs no masking)
+template <int RB>
+__device__ __forceinline__ bool max_check(const float (&x)[RB][4], float (&lmx)[RB], const WaveState<RB>& ws) {
   bool bump = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     lmx[rb] = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
-    bump = bump | (lmx[rb] > ws.m[rb] + kLazyLog2);
+    bump = bump | (lmx[rb] * ws.c > ws.m[rb] + kLazyLog2);
   }
   return __any(bump);
+}
+template <int RB, bool WIN, bool SKIP = true>
+__device__ __forceinline__ bool mask_check(float (&x)[RB][4], float (&lmx)[RB], const WaveState<RB>& ws,
+                                           const RowMask<RB, WIN>& mk, int lane, int t0) {
+  apply_mask<RB, WIN, SKIP>(x, mk, lane, t0);
+  return max_check<RB>(x, lmx, ws);
 }
 
 template <int RB>
@@ -204,6 +207,7 @@ __device__ __forceinline__ void move_ref(const float (&lmx)[RB], WaveState<RB>& 
     float mx = lmx[rb];
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx *= ws.c;
     const bool bump = mx > ws.m[rb] + kLazyLog2;
     const float mnew = bump ? mx : ws.m[rb];
     alpha[rb] = bump ? exp2_fast(ws.m[rb] - mnew) : 1.f;  // m = -inf -> 0
@@ -219,7 +223,7 @@ __device__ __forceinline__ void softmax_p(const float (&x)[RB][4], const WaveSta
     const float ref = (ws.m[rb] == -INFINITY) ? 0.f : ws.m[rb];
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[rb][i] - ref);
+    for (int i = 0; i < 4; ++i) p[i] = exp2_fast(__builtin_fmaf(x[rb][i], ws.c, -ref));
     lsum[rb] = (p[0] + p[1]) + (p[2] + p[3]);
     pb[rb] = half4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
   }
@@ -414,23 +418,56 @@ __device__ __forceinline__ void ring_read8(u32x4 (&d)[8], uint32_t addr) {
 // at t*512 + 16c. K's chunks are permuted inside each token row: chunk c of
 // token t sits at position c ^ (t & 3), so that the MFMA operand reads (lane =
 // token t, chunk 4s + lane/16) of 16 lanes spread over the LDS banks.
+// The copies go through a buffer resource made per half-step (scalar
+// instructions: base = the half-step's first byte, 8 KB long; 4 KB for FP8
+// bytes) with a 32-bit
+// per-lane offset, which the instruction takes as is, so a step's 16 DMAs
+// cost no vector address arithmetic (a 64-bit add each as global loads).
+// Block j's offset is 1024 j plus a per-lane part that depends only on the
+// parity of j (the swizzle). The instruction's offset field (12 bits) is
+// added to both the source and the LDS address, its scalar offset to the
+// source only (pinned with a probe on the GPU); so block j takes (j & 3) *
+// 1024 in the offset field, from j = 4 on 4096 more in the scalar offset,
+// and is given the LDS base ring + (j & 4) * 1024. A lane offset outside the
+// resource's range would read zeros instead of faulting.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer access (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t half_step_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 8192, kRsrcWord3);
+}
+template <int J>
+__device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t r, char* ring, uint32_t lane_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SV_LP(ring + (J & 4) * 1024), 16, lane_off, J >= 4 ? 4096 : 0,
+                                           (J & 3) * 1024, 0);
+}
 template <int B0, int B1>
 __device__ __forceinline__ void dma_k(const _Float16* kb, char* ring, int lane) {
-#pragma unroll
-  for (int j = B0; j < B1; ++j) {
-    const int t = 2 * j + (lane >> 5);
-    const int c = (lane & 31) ^ (t & 3);
-    __builtin_amdgcn_global_load_lds(SV_GP(kb + t * kHeadDim + 8 * c), SV_LP(ring + j * 1024), 16, 0, 0);
-  }
+  const __amdgpu_buffer_rsrc_t r = half_step_rsrc(kb);
+  const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
+  // token t = 2j + h of block j, 16-byte chunk c at chunk c ^ (t & 3)
+  const uint32_t even = h * 512u + 16u * (c ^ h), odd = h * 512u + 16u * (c ^ (2u + h));
+  if constexpr (B0 <= 0 && 0 < B1) dma_block<0>(r, ring, even);
+  if constexpr (B0 <= 1 && 1 < B1) dma_block<1>(r, ring, odd);
+  if constexpr (B0 <= 2 && 2 < B1) dma_block<2>(r, ring, even);
+  if constexpr (B0 <= 3 && 3 < B1) dma_block<3>(r, ring, odd);
+  if constexpr (B0 <= 4 && 4 < B1) dma_block<4>(r, ring, even);
+  if constexpr (B0 <= 5 && 5 < B1) dma_block<5>(r, ring, odd);
+  if constexpr (B0 <= 6 && 6 < B1) dma_block<6>(r, ring, even);
+  if constexpr (B0 <= 7 && 7 < B1) dma_block<7>(r, ring, odd);
 }
 template <int B0, int B1>
 __device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) {
-#pragma unroll
-  for (int j = B0; j < B1; ++j) {
-    const int t = 2 * j + (lane >> 5);
-    const int c = (lane & 31) ^ (2 * (t & 3));
-    __builtin_amdgcn_global_load_lds(SV_GP(vb + t * kHeadDim + 8 * c), SV_LP(ring + j * 1024), 16, 0, 0);
-  }
+  const __amdgpu_buffer_rsrc_t r = half_step_rsrc(vb);
+  const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
+  // token t = 2j + h of block j, 16-byte chunk c at chunk c ^ 2 (t & 3)
+  const uint32_t even = h * 512u + 16u * (c ^ (2u * h)), odd = h * 512u + 16u * (c ^ (4u + 2u * h));
+  if constexpr (B0 <= 0 && 0 < B1) dma_block<0>(r, ring, even);
+  if constexpr (B0 <= 1 && 1 < B1) dma_block<1>(r, ring, odd);
+  if constexpr (B0 <= 2 && 2 < B1) dma_block<2>(r, ring, even);
+  if constexpr (B0 <= 3 && 3 < B1) dma_block<3>(r, ring, odd);
+  if constexpr (B0 <= 4 && 4 < B1) dma_block<4>(r, ring, even);
+  if constexpr (B0 <= 5 && 5 < B1) dma_block<5>(r, ring, odd);
+  if constexpr (B0 <= 6 && 6 < B1) dma_block<6>(r, ring, even);
+  if constexpr (B0 <= 7 && 7 < B1) dma_block<7>(r, ring, odd);
 }
 // The same read into accumulation registers: for fragments that only feed
 // matrix ops (which read A/B operands from them), keeping them out of the
@@ -515,21 +552,28 @@ constexpr int kStage8 = 8448;
 // V scales (lanes 32..63).
 __device__ __forceinline__ void dma_k8(const uint8_t* kb, const _Float16* ksb, const _Float16* vsb,
                                        char* stage, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = 4 * j + (lane >> 4);
-    const int c = (lane & 15) ^ (t & 3);
-    __builtin_amdgcn_global_load_lds(SV_GP(kb + t * kHeadDim + 16 * c), SV_LP(stage + j * 1024), 16, 0, 0);
-  }
+  // (a buffer resource over the 4 KB, as for fp16: token t = 4j + l/16,
+  // whose t & 3 does not depend on j, so one lane offset serves all blocks)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kb), (short)0, 4096,
+                                                                     kRsrcWord3);
+  const uint32_t g = (uint32_t)lane >> 4;
+  const uint32_t off = g * 256u + 16u * (((uint32_t)lane & 15u) ^ (g & 3u));
+  dma_block<0>(r, stage, off);
+  dma_block<1>(r, stage, off);
+  dma_block<2>(r, stage, off);
+  dma_block<3>(r, stage, off);
   const _Float16* ssrc = lane < 32 ? ksb + 2 * lane : vsb + 2 * (lane - 32);
   __builtin_amdgcn_global_load_lds(SV_GP(ssrc), SV_LP(stage + 8192), 4, 0, 0);
 }
 // V half-step of an FP8 step: the 4 KB of 16 tokens copied as is.
 __device__ __forceinline__ void dma_v8(const uint8_t* vb, char* stage, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_global_load_lds(SV_GP(vb + (j * kWave + lane) * 16), SV_LP(stage + 4096 + j * 1024), 16,
-                                     0, 0);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), (short)0, 4096,
+                                                                     kRsrcWord3);
+  const uint32_t off = (uint32_t)lane * 16u;
+  dma_block<0>(r, stage + 4096, off);
+  dma_block<1>(r, stage + 4096, off);
+  dma_block<2>(r, stage + 4096, off);
+  dma_block<3>(r, stage + 4096, off);
 }
 // Per-lane offsets: K block bk (bytes 64bk + 16*(l/16) of token l%16) at
 // k8_lane_off + 64*bk; V dword 4e+bb (bytes 64bb + 4*(l%16) of token
@@ -587,15 +631,14 @@ __device__ __forceinline__ void ring_read_v8(VFrag8& f, uint32_t addr) {
       : "memory");
 }
 
-// The scaled scores of one FP8 step: per 64-channel block, two matrix ops
-// on the converted K and the wave's Q fragments (in registers), one
-// accumulator per (row block, scale block) so the block scales are applied
-// after all matrix ops are issued: S = sum_b scale_b * partial_b, one
-// multiply and three fused multiply-adds per score, the softmax scale applied
-// once at the end.
+// The raw scores of one FP8 step: per 64-channel block, two matrix ops on
+// the converted K and the wave's Q fragments (in registers), one accumulator
+// per (row block, scale block) so the block scales are applied after all
+// matrix ops are issued: S = sum_b scale_b * partial_b, one multiply and
+// three fused multiply-adds per score (the softmax scale enters with the
+// exponent).
 template <int RB>
-__device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4 (&qa)[RB][8], float scale_log2,
-                                             float (&x)[RB][4]) {
+__device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4 (&qa)[RB][8], float (&x)[RB][4]) {
   u32x4 kc[8];
 #pragma unroll
   for (int bk = 0; bk < 4; ++bk) {
@@ -625,8 +668,7 @@ __device__ __forceinline__ void scores8_mfma(const KFrag8& kf, const u32x4 (&qa)
       float t = fk[i][0] * acc[rb][0][i];
       t = __builtin_fmaf(fk[i][1], acc[rb][1][i], t);
       t = __builtin_fmaf(fk[i][2], acc[rb][2][i], t);
-      t = __builtin_fmaf(fk[i][3], acc[rb][3][i], t);
-      x[rb][i] = t * scale_log2;
+      x[rb][i] = __builtin_fmaf(fk[i][3], acc[rb][3][i], t);
     }
 }
 
