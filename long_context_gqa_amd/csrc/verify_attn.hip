@@ -365,7 +365,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         sv[0] = kf.sv[0];
         sv[1] = kf.sv[1];
       }
-      for (int kk = 0; kk + 1 < nb; ++kk) {
+      auto body = [&](int kk, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         const int t0 = step_t0(kk);
         VFrag8 vf;
         ring_read_v8<kWaitV>(vf, sbase(kk) + 4096 + v8_lane_off(lane));
@@ -379,7 +380,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         step_pv8<RB, false>(vf, sv, pr, ws, lane, t0, kv);
         sv[0] = kf.sv[0];
         sv[1] = kf.sv[1];
-        const bool any = mask_check<RB>(x, lmx, ws, mk, lane, step_t0(kk + 1));
+        bool any;
+        if constexpr (MASKED) any = mask_check<RB>(x, lmx, ws, mk, lane, step_t0(kk + 1));
+        else any = max_check<RB>(x, lmx, ws);
         softmax_p<RB>(x, ws, lsum, pr);
         pin_softmax<RB>(pr, lsum);
 #pragma unroll
@@ -391,7 +394,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) ws.l[rb] = ws.l[rb] * alpha[rb] + lsum[rb];
         if (any) rescale_o<RB>(ws, alpha);
+      };
+      // full attention: masking only on the wave's last steps (as in the
+      // fp16 loop below)
+      int kk = 0, clean = 0;
+      if constexpr (!WIN) {
+        const int span = mk.lim_min - kStep - step_t0(1);
+        clean = span < 0 ? 0 : min(nb - 1, span / (kStep * NTS) + 1);
       }
+      for (; kk < clean; ++kk) body(kk, std::false_type{});
+      for (; kk + 1 < nb; ++kk) body(kk, std::true_type{});
       {
         VFrag8 vf;
         ring_read_v8<kWaitV>(vf, sbase(nb - 1) + 4096 + v8_lane_off(lane));
