@@ -506,8 +506,12 @@ def measured_traffic(path, workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, rec["source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    # the kernel's source files, hashed in the listed order as one byte string
+    h = hashlib.sha256()
+    for src in rec.get("sources") or [rec["source"]]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["source_sha256"]:
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
