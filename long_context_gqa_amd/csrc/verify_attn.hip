@@ -56,6 +56,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   static_assert(!CLAIM || (!FP8 && DEPTH == 1 && !WIN), "claimed work: fp16 KV, one step in flight, full attention");
   using SM = Smem<RB, FP8, DEPTH>;
   constexpr int NTS = kWavesPerGroup;  // waves that split the chunk's steps
+  // K/V cache policy: two steps in flight is the launch whose row tiles share
+  // the keys (through L2); with one row tile every K/V byte is read once.
+  constexpr int CP = DEPTH == 1 ? kCacheStream : kCacheDefault;
   __shared__ __attribute__((aligned(1024))) unsigned char qsm[SM::QBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char bigsm[SM::BIG];
   __shared__ float s_m[NTS][RB * 16];
@@ -265,11 +268,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       const size_t tr = tok_row(rows_first, min(d, nb0 - 1));
       char* stage = ring + d * kStageBytes;
       if constexpr (FP8) {
-        dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, stage, lane);
-        dma_v8(vpool8 + tr * kHeadDim, stage, lane);
+        dma_k8<CP>(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, stage, lane);
+        dma_v8<CP>(vpool8 + tr * kHeadDim, stage, lane);
       } else {
-        dma_k<0, 8>(kpool + tr * kHeadDim, stage, lane);
-        dma_v<0, 8>(vpool + tr * kHeadDim, stage + 8192, lane);
+        dma_k<0, 8, CP>(kpool + tr * kHeadDim, stage, lane);
+        dma_v<0, 8, CP>(vpool + tr * kHeadDim, stage + 8192, lane);
       }
     }
   }
@@ -331,10 +334,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       auto step_t0 = [&](int kk) { return live_t0(ts + (bstart + kk) * NTS); };
       auto issue_k = [&](int kk, int stg) {
         const size_t tr = tok_row(rows, kk);
-        dma_k8(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring + stg * kStage8, lane);
+        dma_k8<CP>(kpool8 + tr * kHeadDim, a.k_scales + tr * 4, a.v_scales + tr * 4, ring + stg * kStage8, lane);
       };
       auto issue_v = [&](int kk, int stg) {
-        dma_v8(vpool8 + tok_row(rows, kk) * kHeadDim, ring + stg * kStage8, lane);
+        dma_v8<CP>(vpool8 + tok_row(rows, kk) * kHeadDim, ring + stg * kStage8, lane);
       };
       if (bstart > 0) {  // (the first batch's first steps were issued before Q staging)
 #pragma unroll
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         {
           KFrag kf;
           ring_read8<kWait, 64>(kf.k, ring_lds + k_lane_off(lane));
-          dma_k<0, 8>(kpool + tgt(1) * kHeadDim, ring, lane);
+          dma_k<0, 8, CP>(kpool + tgt(1) * kHeadDim, ring, lane);
           step_scores<RB>(kf, qa, ws, pb, lane, kStep * base, mk);
         }
         for (;;) {
@@ -476,14 +479,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
             }
           }
           __builtin_amdgcn_sched_barrier(0);
-          dma_v<0, 8>(vpool + tgt(kk + 1) * kHeadDim, ring + 8192, lane);
+          dma_v<0, 8, CP>(vpool + tgt(kk + 1) * kHeadDim, ring + 8192, lane);
           KFrag kf;
           // (two more operations are newer than K's DMAs after a first step)
           if (first)
             ring_read8_acc<kWait + 2, 64>(kf.k, ring_lds + k_lane_off(lane));
           else
             ring_read8_acc<kWait, 64>(kf.k, ring_lds + k_lane_off(lane));
-          dma_k<0, 8>(kpool + tgt(kk + 2) * kHeadDim, ring, lane);
+          dma_k<0, 8, CP>(kpool + tgt(kk + 2) * kHeadDim, ring, lane);
           float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
           scores_mfma<RB>(kf, qa, x);
           // (only the stream's last step can end above kv_len)
@@ -548,8 +551,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
           const int kd = min(d, nb - 1);
-          dma_k<0, 8>(step_base(kd, kpool), ring + d * kRingStage, lane);
-          dma_v<0, 8>(step_base(kd, vpool), ring + d * kRingStage + 8192, lane);
+          dma_k<0, 8, CP>(step_base(kd, kpool), ring + d * kRingStage, lane);
+          dma_v<0, 8, CP>(step_base(kd, vpool), ring + d * kRingStage + 8192, lane);
         }
       }
       constexpr int kWait = 8 * (2 * DEPTH - 1);
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
       {
         KFrag kf;
         ring_read8<kWait, 64>(kf.k, ring_lds + stage(0) + k_lane_off(lane));
-        dma_k<0, 8>(step_base(min(DEPTH, nb - 1), kpool), ring + stage(0), lane);
+        dma_k<0, 8, CP>(step_base(min(DEPTH, nb - 1), kpool), ring + stage(0), lane);
         step_scores<RB>(kf, qa, ws, pb, lane, step_t0(0), mk);
       }
       auto body = [&](int kk, auto masked) {
@@ -570,10 +573,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
         const int st = stage(kk), st1 = stage(kk + 1);
         VFrag vf;
         ring_read_vt<kWait>(vf, ring_lds + st + 8192 + v_lane_off(lane), lane);
-        dma_v<0, 8>(step_base(min(kk + DEPTH, nb - 1), vpool), ring + st + 8192, lane);
+        dma_v<0, 8, CP>(step_base(min(kk + DEPTH, nb - 1), vpool), ring + st + 8192, lane);
         KFrag kf;
         ring_read8_acc<kWait, 64>(kf.k, ring_lds + st1 + k_lane_off(lane));
-        dma_k<0, 8>(step_base(min(kk + 1 + DEPTH, nb - 1), kpool), ring + st1, lane);
+        dma_k<0, 8, CP>(step_base(min(kk + 1 + DEPTH, nb - 1), kpool), ring + st1, lane);
         float x[RB][4], lmx[RB], alpha[RB], lsum[RB];
         scores_mfma<RB>(kf, qa, x);
         // (a step before the wave's last of the batch ends below kv_len)

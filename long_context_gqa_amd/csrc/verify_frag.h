@@ -430,44 +430,55 @@ __device__ __forceinline__ void ring_read8(u32x4 (&d)[8], uint32_t addr) {
 // 1024 in the offset field, from j = 4 on 4096 more in the scalar offset,
 // and is given the LDS base ring + (j & 4) * 1024. A lane offset outside the
 // resource's range would read zeros instead of faulting.
+//
+// Cache policy of the copies (the instruction's cache-policy field): bytes
+// that only one workgroup reads go non-temporal (kCacheStream, the nt bit),
+// the rest with the default policy. On MI355X a page gather in this kernel's
+// order (random 8 KB pages, 16 KB per wave step, one step in flight) streams
+// at 6.95 TB/s with the nt bit against 6.16 TB/s without it (a standalone
+// probe; the scope bits sc0/sc1 change nothing). Where several row tiles read
+// the same keys (the later ones from L2), nt costs more than it gains: the
+// lines leave L2 before the second reader comes.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;  // nt
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer access (gfx9 family)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t half_step_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 8192, kRsrcWord3);
 }
-template <int J>
+template <int J, int CP>
 __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t r, char* ring, uint32_t lane_off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SV_LP(ring + (J & 4) * 1024), 16, lane_off, J >= 4 ? 4096 : 0,
-                                           (J & 3) * 1024, 0);
+                                           (J & 3) * 1024, CP);
 }
-template <int B0, int B1>
+template <int B0, int B1, int CP>
 __device__ __forceinline__ void dma_k(const _Float16* kb, char* ring, int lane) {
   const __amdgpu_buffer_rsrc_t r = half_step_rsrc(kb);
   const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
   // token t = 2j + h of block j, 16-byte chunk c at chunk c ^ (t & 3)
   const uint32_t even = h * 512u + 16u * (c ^ h), odd = h * 512u + 16u * (c ^ (2u + h));
-  if constexpr (B0 <= 0 && 0 < B1) dma_block<0>(r, ring, even);
-  if constexpr (B0 <= 1 && 1 < B1) dma_block<1>(r, ring, odd);
-  if constexpr (B0 <= 2 && 2 < B1) dma_block<2>(r, ring, even);
-  if constexpr (B0 <= 3 && 3 < B1) dma_block<3>(r, ring, odd);
-  if constexpr (B0 <= 4 && 4 < B1) dma_block<4>(r, ring, even);
-  if constexpr (B0 <= 5 && 5 < B1) dma_block<5>(r, ring, odd);
-  if constexpr (B0 <= 6 && 6 < B1) dma_block<6>(r, ring, even);
-  if constexpr (B0 <= 7 && 7 < B1) dma_block<7>(r, ring, odd);
+  if constexpr (B0 <= 0 && 0 < B1) dma_block<0, CP>(r, ring, even);
+  if constexpr (B0 <= 1 && 1 < B1) dma_block<1, CP>(r, ring, odd);
+  if constexpr (B0 <= 2 && 2 < B1) dma_block<2, CP>(r, ring, even);
+  if constexpr (B0 <= 3 && 3 < B1) dma_block<3, CP>(r, ring, odd);
+  if constexpr (B0 <= 4 && 4 < B1) dma_block<4, CP>(r, ring, even);
+  if constexpr (B0 <= 5 && 5 < B1) dma_block<5, CP>(r, ring, odd);
+  if constexpr (B0 <= 6 && 6 < B1) dma_block<6, CP>(r, ring, even);
+  if constexpr (B0 <= 7 && 7 < B1) dma_block<7, CP>(r, ring, odd);
 }
-template <int B0, int B1>
+template <int B0, int B1, int CP>
 __device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) {
   const __amdgpu_buffer_rsrc_t r = half_step_rsrc(vb);
   const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
   // token t = 2j + h of block j, 16-byte chunk c at chunk c ^ 2 (t & 3)
   const uint32_t even = h * 512u + 16u * (c ^ (2u * h)), odd = h * 512u + 16u * (c ^ (4u + 2u * h));
-  if constexpr (B0 <= 0 && 0 < B1) dma_block<0>(r, ring, even);
-  if constexpr (B0 <= 1 && 1 < B1) dma_block<1>(r, ring, odd);
-  if constexpr (B0 <= 2 && 2 < B1) dma_block<2>(r, ring, even);
-  if constexpr (B0 <= 3 && 3 < B1) dma_block<3>(r, ring, odd);
-  if constexpr (B0 <= 4 && 4 < B1) dma_block<4>(r, ring, even);
-  if constexpr (B0 <= 5 && 5 < B1) dma_block<5>(r, ring, odd);
-  if constexpr (B0 <= 6 && 6 < B1) dma_block<6>(r, ring, even);
-  if constexpr (B0 <= 7 && 7 < B1) dma_block<7>(r, ring, odd);
+  if constexpr (B0 <= 0 && 0 < B1) dma_block<0, CP>(r, ring, even);
+  if constexpr (B0 <= 1 && 1 < B1) dma_block<1, CP>(r, ring, odd);
+  if constexpr (B0 <= 2 && 2 < B1) dma_block<2, CP>(r, ring, even);
+  if constexpr (B0 <= 3 && 3 < B1) dma_block<3, CP>(r, ring, odd);
+  if constexpr (B0 <= 4 && 4 < B1) dma_block<4, CP>(r, ring, even);
+  if constexpr (B0 <= 5 && 5 < B1) dma_block<5, CP>(r, ring, odd);
+  if constexpr (B0 <= 6 && 6 < B1) dma_block<6, CP>(r, ring, even);
+  if constexpr (B0 <= 7 && 7 < B1) dma_block<7, CP>(r, ring, odd);
 }
 // The same read into accumulation registers: for fragments that only feed
 // matrix ops (which read A/B operands from them), keeping them out of the
@@ -550,6 +561,7 @@ constexpr int kStage8 = 8448;
 // read contiguously, chunk c (16 bytes) of token t at position c ^ (t & 3);
 // plus one 256-byte block holding the 16 tokens' K scales (lanes 0..31) and
 // V scales (lanes 32..63).
+template <int CP>
 __device__ __forceinline__ void dma_k8(const uint8_t* kb, const _Float16* ksb, const _Float16* vsb,
                                        char* stage, int lane) {
   // (a buffer resource over the 4 KB, as for fp16: token t = 4j + l/16,
@@ -558,22 +570,23 @@ __device__ __forceinline__ void dma_k8(const uint8_t* kb, const _Float16* ksb, c
                                                                      kRsrcWord3);
   const uint32_t g = (uint32_t)lane >> 4;
   const uint32_t off = g * 256u + 16u * (((uint32_t)lane & 15u) ^ (g & 3u));
-  dma_block<0>(r, stage, off);
-  dma_block<1>(r, stage, off);
-  dma_block<2>(r, stage, off);
-  dma_block<3>(r, stage, off);
+  dma_block<0, CP>(r, stage, off);
+  dma_block<1, CP>(r, stage, off);
+  dma_block<2, CP>(r, stage, off);
+  dma_block<3, CP>(r, stage, off);
   const _Float16* ssrc = lane < 32 ? ksb + 2 * lane : vsb + 2 * (lane - 32);
-  __builtin_amdgcn_global_load_lds(SV_GP(ssrc), SV_LP(stage + 8192), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(SV_GP(ssrc), SV_LP(stage + 8192), 4, 0, CP);
 }
 // V half-step of an FP8 step: the 4 KB of 16 tokens copied as is.
+template <int CP>
 __device__ __forceinline__ void dma_v8(const uint8_t* vb, char* stage, int lane) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), (short)0, 4096,
                                                                      kRsrcWord3);
   const uint32_t off = (uint32_t)lane * 16u;
-  dma_block<0>(r, stage + 4096, off);
-  dma_block<1>(r, stage + 4096, off);
-  dma_block<2>(r, stage + 4096, off);
-  dma_block<3>(r, stage + 4096, off);
+  dma_block<0, CP>(r, stage + 4096, off);
+  dma_block<1, CP>(r, stage + 4096, off);
+  dma_block<2, CP>(r, stage + 4096, off);
+  dma_block<3, CP>(r, stage + 4096, off);
 }
 // Per-lane offsets: K block bk (bytes 64bk + 16*(l/16) of token l%16) at
 // k8_lane_off + 64*bk; V dword 4e+bb (bytes 64bb + 4*(l%16) of token
