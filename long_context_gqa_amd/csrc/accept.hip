@@ -43,7 +43,7 @@ __device__ __forceinline__ Best wave_best(Best x) {
 
 }  // namespace
 
-template <bool VEC4>
+template <bool VEC4, bool NT>
 __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* __restrict__ logits,
                                                                   int vocab, int slice,
                                                                   int n_slices, float2* ws,
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* _
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = lo + 4 * (threadIdx.x + u * kThreads);
-      v[u] = c < hi ? *reinterpret_cast<const float4*>(rp + c)
+      v[u] = c < hi ? load4<NT>(rp + c)
                     : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
 #pragma unroll
@@ -165,11 +165,15 @@ __global__ __launch_bounds__(kThreads) void accept_finalize_kernel(AcceptLaunch 
 void launch_greedy_accept(const AcceptLaunch& a, hipStream_t s) {
   const int max_rows = a.batch * a.q_len;
   dim3 g1(a.n_slices, max_rows);
-  if (a.vocab % 4 == 0)
-    hipLaunchKernelGGL((argmax_partial_kernel<true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
+  const bool once = (long long)max_rows * a.vocab * (long long)sizeof(float) >= kStreamOnceBytes;
+  if (a.vocab % 4 == 0 && once)
+    hipLaunchKernelGGL((argmax_partial_kernel<true, true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
+                       a.slice, a.n_slices, a.ws, a.q_start, a.batch, max_rows);
+  else if (a.vocab % 4 == 0)
+    hipLaunchKernelGGL((argmax_partial_kernel<true, false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
                        a.slice, a.n_slices, a.ws, a.q_start, a.batch, max_rows);
   else
-    hipLaunchKernelGGL((argmax_partial_kernel<false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
+    hipLaunchKernelGGL((argmax_partial_kernel<false, false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
                        a.slice, a.n_slices, a.ws, a.q_start, a.batch, max_rows);
   hipLaunchKernelGGL(accept_finalize_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
 }

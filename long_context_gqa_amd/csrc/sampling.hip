@@ -73,7 +73,7 @@ __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
 
 }  // namespace
 
-template <bool VEC4>
+template <bool VEC4, bool NT>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(const float* __restrict__ logits, int vocab,
                                                              int slice, int n_slices, float c, float2* ws1) {
   const int sl = blockIdx.x, row = blockIdx.y;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(const float* __rest
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int col = lo + 4 * (threadIdx.x + u * kThreads);
-      v[u] = col < hi ? *reinterpret_cast<const float4*>(rp + col)
+      v[u] = col < hi ? load4<NT>(rp + col)
                       : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
     float m = -INFINITY;
@@ -334,12 +334,17 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(SampleLaunch a) {
 
 void launch_rejection_accept(const SampleLaunch& a, hipStream_t s) {
   dim3 g1(a.n_slices, a.batch * a.q_len), g2(a.n_slices, a.batch);
+  const bool once = (long long)a.batch * a.q_len * a.vocab * (long long)sizeof(float) >= kStreamOnceBytes;
   if (a.vocab % 4 == 0) {
-    hipLaunchKernelGGL((row_stats_kernel<true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.slice, a.n_slices,
-                       a.c, a.ws1);
+    if (once)
+      hipLaunchKernelGGL((row_stats_kernel<true, true>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.slice,
+                         a.n_slices, a.c, a.ws1);
+    else
+      hipLaunchKernelGGL((row_stats_kernel<true, false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.slice,
+                         a.n_slices, a.c, a.ws1);
     hipLaunchKernelGGL((walk_residual_kernel<true>), g2, dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((row_stats_kernel<false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.slice, a.n_slices,
+    hipLaunchKernelGGL((row_stats_kernel<false, false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab, a.slice, a.n_slices,
                        a.c, a.ws1);
     hipLaunchKernelGGL((walk_residual_kernel<false>), g2, dim3(kThreads), 0, s, a);
   }

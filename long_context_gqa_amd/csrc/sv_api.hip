@@ -60,6 +60,7 @@ struct Plan {
   int splits, chunk;   // key chunks and their length in tokens
   bool claim;          // the keys of each (request, KV head) are claimed in grains (splits = slots per group)
   bool balanced;       // XCD-balanced static chunks (splits = slots per group, a multiple of 8)
+  bool stream_once;    // one row tile and a large pass: the K/V copies go non-temporal
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
 
@@ -208,6 +209,12 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   }
   pl->splits = (int)S;
   pl->chunk = (int)chunk;
+  // K/V bytes of the pass if every request were max_kv_len long (or its
+  // window): K and V rows of D channels, plus FP8's scale per 64 channels
+  const long long row_bytes = p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * (sv::kHeadDim + sv::kHeadDim / 64 * 2)
+                                                            : 2LL * sv::kHeadDim * 2;
+  pl->stream_once = pl->row_blocks == 1 &&
+                    (long long)p->batch * p->num_kv_heads * maxkv * row_bytes >= sv::kStreamOnceBytes;
   if (S > 1) {
     const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
     pl->part_o_bytes = align256((size_t)S * rows * sv::kHeadDim * sizeof(float));
@@ -304,7 +311,7 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.window = p->window;
   a.sink = p->sink;
   a.balanced = (pl.balanced && !q_start) ? 1 : 0;
-  sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, claim, s);
+  sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, claim, pl.stream_once, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
   if (pl.splits > 1) {

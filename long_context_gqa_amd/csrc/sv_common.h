@@ -62,6 +62,27 @@ struct MergeArgs {
   int32_t balanced;  // every split slot holds a partial (XCD-balanced static chunks)
 };
 
+// Cache policy of one-pass streams (the K/V of a verify pass read by one
+// workgroup each, the logit scans). A pass of at least kStreamOnceBytes reads
+// non-temporally (the nt bit): on MI355X such a stream reads measurably faster
+// that way (a page gather in the verify kernel's order: 6.95 against 6.16
+// TB/s). A smaller pass keeps the default policy, under which the 256 MB
+// Infinity Cache can keep its bytes for the next reader (read again and again,
+// a 17 MB verify pass and an 8 MB logit scan are a few percent slower with
+// the nt bit).
+constexpr long long kStreamOnceBytes = 32LL << 20;
+
+// a 16-byte load, non-temporal when NT
+template <bool NT>
+__device__ __forceinline__ float4 load4(const float* p) {
+  if constexpr (NT) {
+    const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+
 // Length of request b as the kernels use it: the stored value clamped to the
 // host bound and to what the page table can address. Shared by the attention
 // and merge kernels so both see the same number of chunks.
@@ -169,7 +190,7 @@ __host__ __device__ inline int xcd_chunk_start(int total, int s, int S) {
   return (int)(((long long)total * (1000LL * s + kXcdWeight * (s & 1))) / (1000LL * S));
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, bool claim, hipStream_t s);
+void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, bool claim, bool stream_once, hipStream_t s);
 void launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace sv

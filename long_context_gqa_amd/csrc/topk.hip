@@ -256,7 +256,7 @@ __device__ __forceinline__ void slice_wave_topk(const float (&v)[NPL], int lo, i
 // they fit one per lane, sorted once by wave 0. Otherwise (many values tied
 // or clustered) each wave finds its best k with the per-wave threshold of
 // slice_wave_topk and wave 0 merges the 4k winners.
-template <bool VEC4, int NPL>
+template <bool VEC4, int NPL, bool NT>
 __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __restrict__ logits, int vocab, int k,
                                                               int n_slices, float2* ws) {
   const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float* __res
 #pragma unroll
     for (int g = 0; g < NPL / 4; ++g) {
       const int col = slice_col(lo, tid, 4 * g);
-      const float4 x = col < hi ? *reinterpret_cast<const float4*>(rp + col)
+      const float4 x = col < hi ? load4<NT>(rp + col)
                                 : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       v[4 * g] = x.x;
       v[4 * g + 1] = x.y;
@@ -373,17 +373,24 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const float2* __re
 void launch_topk(const TopkLaunch& a, hipStream_t s) {
   dim3 g1(a.n_slices, a.rows);
   const bool vec4 = a.vocab % 4 == 0, wide = a.slice == kTopkSliceWide;
-  if (vec4 && wide)
-    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSliceWide / kThreads>), g1, dim3(kThreads), 0, s, a.logits,
+  const bool once = (long long)a.rows * a.vocab * (long long)sizeof(float) >= kStreamOnceBytes;
+  if (vec4 && wide && once)
+    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSliceWide / kThreads, true>), g1, dim3(kThreads), 0, s,
+                       a.logits, a.vocab, a.k, a.n_slices, a.ws);
+  else if (vec4 && wide)
+    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSliceWide / kThreads, false>), g1, dim3(kThreads), 0, s,
+                       a.logits, a.vocab, a.k, a.n_slices, a.ws);
+  else if (vec4 && once)
+    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSlice / kThreads, true>), g1, dim3(kThreads), 0, s, a.logits,
                        a.vocab, a.k, a.n_slices, a.ws);
   else if (vec4)
-    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSlice / kThreads>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
+    hipLaunchKernelGGL((topk_slice_kernel<true, kTopkSlice / kThreads, false>), g1, dim3(kThreads), 0, s, a.logits, a.vocab,
                        a.k, a.n_slices, a.ws);
   else if (wide)
-    hipLaunchKernelGGL((topk_slice_kernel<false, kTopkSliceWide / kThreads>), g1, dim3(kThreads), 0, s, a.logits,
+    hipLaunchKernelGGL((topk_slice_kernel<false, kTopkSliceWide / kThreads, false>), g1, dim3(kThreads), 0, s, a.logits,
                        a.vocab, a.k, a.n_slices, a.ws);
   else
-    hipLaunchKernelGGL((topk_slice_kernel<false, kTopkSlice / kThreads>), g1, dim3(kThreads), 0, s, a.logits,
+    hipLaunchKernelGGL((topk_slice_kernel<false, kTopkSlice / kThreads, false>), g1, dim3(kThreads), 0, s, a.logits,
                        a.vocab, a.k, a.n_slices, a.ws);
   hipLaunchKernelGGL(topk_merge_kernel, dim3((a.rows + kWavesPerGroup - 1) / kWavesPerGroup), dim3(kThreads), 0, s,
                      a.ws, a.rows, a.n_slices, a.k, a.out_ids, a.out_vals);

@@ -50,15 +50,16 @@ struct Smem {
   static constexpr int BIG = RBYTES > OBYTES ? RBYTES : OBYTES;
 };
 
-template <int RB, bool FP8, int DEPTH, bool WIN, bool CLAIM>
+template <int RB, bool FP8, int DEPTH, bool WIN, bool CLAIM, int CP>
 __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   static_assert(DEPTH == 1 || DEPTH == 2, "one or two steps in flight");
   static_assert(!CLAIM || (!FP8 && DEPTH == 1 && !WIN), "claimed work: fp16 KV, one step in flight, full attention");
   using SM = Smem<RB, FP8, DEPTH>;
   constexpr int NTS = kWavesPerGroup;  // waves that split the chunk's steps
-  // K/V cache policy: two steps in flight is the launch whose row tiles share
-  // the keys (through L2); with one row tile every K/V byte is read once.
-  constexpr int CP = DEPTH == 1 ? kCacheStream : kCacheDefault;
+  // K/V cache policy CP: two steps in flight is the launch whose row tiles
+  // share the keys (the later ones read them from L2), which keeps the default
+  // policy; with one row tile every K/V byte is read once.
+  static_assert(DEPTH == 1 || CP == kCacheDefault, "row tiles that share keys keep them in L2");
   __shared__ __attribute__((aligned(1024))) unsigned char qsm[SM::QBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char bigsm[SM::BIG];
   __shared__ float s_m[NTS][RB * 16];
@@ -759,42 +760,47 @@ __global__ __launch_bounds__(kThreads, 1) void verify_attn_kernel(AttnArgs a) {
   if (tid == 0 && s_flag && a.flags) atomicOr(a.flags, s_flag);
 }
 
-template <bool FP8, int DEPTH, bool WIN>
+template <bool FP8, int DEPTH, bool WIN, int CP>
 void launch_rb(const AttnArgs& a, int rb, dim3 grid, hipStream_t s) {
   const dim3 block(kThreads);
-  if (rb == 1 && DEPTH == 1) hipLaunchKernelGGL((verify_attn_kernel<1, FP8, 1, WIN, false>), grid, block, 0, s, a);
-  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, FP8, DEPTH, WIN, false>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((verify_attn_kernel<3, FP8, DEPTH, WIN, false>), grid, block, 0, s, a);
+  if (rb == 1 && DEPTH == 1) hipLaunchKernelGGL((verify_attn_kernel<1, FP8, 1, WIN, false, CP>), grid, block, 0, s, a);
+  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, FP8, DEPTH, WIN, false, CP>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((verify_attn_kernel<3, FP8, DEPTH, WIN, false, CP>), grid, block, 0, s, a);
 }
 
-// claimed work: fp16 KV, full attention, one row tile, blocks of one width
+// claimed work: fp16 KV, full attention, one row tile, blocks of one width;
+// taken for long requests only (at least 32K keys per KV head), whose keys
+// are read once
 void launch_claim(const AttnArgs& a, int rb, hipStream_t s) {
   const dim3 grid(a.units), block(kThreads);
-  if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false, 1, false, true>), grid, block, 0, s, a);
-  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false, 1, false, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((verify_attn_kernel<3, false, 1, false, true>), grid, block, 0, s, a);
+  constexpr int CP = kCacheStream;
+  if (rb == 1) hipLaunchKernelGGL((verify_attn_kernel<1, false, 1, false, true, CP>), grid, block, 0, s, a);
+  else if (rb == 2) hipLaunchKernelGGL((verify_attn_kernel<2, false, 1, false, true, CP>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((verify_attn_kernel<3, false, 1, false, true, CP>), grid, block, 0, s, a);
 }
 
 template <bool FP8, bool WIN>
-void launch_depth(const AttnArgs& a, int rb, hipStream_t s) {
+void launch_depth(const AttnArgs& a, int rb, bool stream_once, hipStream_t s) {
   // one workgroup per unit; with n row tiles, 8n ids per 8 units, and the
   // workgroups on the same keys (rb is then 2 or 3) keep two steps in flight
   if (a.row_blocks > 1)
-    launch_rb<FP8, 2, WIN>(a, rb, dim3(a.row_blocks * ((a.units + 7) / 8 * 8)), s);
+    launch_rb<FP8, 2, WIN, kCacheDefault>(a, rb, dim3(a.row_blocks * ((a.units + 7) / 8 * 8)), s);
+  else if (stream_once)
+    launch_rb<FP8, 1, WIN, kCacheStream>(a, rb, dim3(a.units), s);
   else
-    launch_rb<FP8, 1, WIN>(a, rb, dim3(a.units), s);
+    launch_rb<FP8, 1, WIN, kCacheDefault>(a, rb, dim3(a.units), s);
 }
 
-void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, bool claim, hipStream_t s) {
+void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, bool claim, bool stream_once, hipStream_t s) {
   const bool win = a.window > 0;
   if (claim) {
     launch_claim(a, rb, s);
   } else if (fp8) {
-    if (win) launch_depth<true, true>(a, rb, s);
-    else launch_depth<true, false>(a, rb, s);
+    if (win) launch_depth<true, true>(a, rb, stream_once, s);
+    else launch_depth<true, false>(a, rb, stream_once, s);
   } else {
-    if (win) launch_depth<false, true>(a, rb, s);
-    else launch_depth<false, false>(a, rb, s);
+    if (win) launch_depth<false, true>(a, rb, stream_once, s);
+    else launch_depth<false, false>(a, rb, stream_once, s);
   }
 }
 

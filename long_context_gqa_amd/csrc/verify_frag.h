@@ -431,14 +431,15 @@ __device__ __forceinline__ void ring_read8(u32x4 (&d)[8], uint32_t addr) {
 // and is given the LDS base ring + (j & 4) * 1024. A lane offset outside the
 // resource's range would read zeros instead of faulting.
 //
-// Cache policy of the copies (the instruction's cache-policy field): bytes
-// that only one workgroup reads go non-temporal (kCacheStream, the nt bit),
-// the rest with the default policy. On MI355X a page gather in this kernel's
-// order (random 8 KB pages, 16 KB per wave step, one step in flight) streams
-// at 6.95 TB/s with the nt bit against 6.16 TB/s without it (a standalone
-// probe; the scope bits sc0/sc1 change nothing). Where several row tiles read
-// the same keys (the later ones from L2), nt costs more than it gains: the
-// lines leave L2 before the second reader comes.
+// Cache policy of the copies (the instruction's cache-policy field): a pass
+// whose keys one workgroup each reads, and that is large (kStreamOnceBytes),
+// goes non-temporal (kCacheStream, the nt bit), the rest with the default
+// policy. On MI355X a page gather in this kernel's order (random 8 KB pages,
+// 16 KB per wave step, one step in flight) streams at 6.95 TB/s with the nt
+// bit against 6.16 TB/s without it (a standalone probe; the scope bits
+// sc0/sc1 change nothing). Where several row tiles read the same keys (the
+// later ones from L2), nt costs more than it gains: the lines leave L2
+// before the second reader comes.
 constexpr int kCacheDefault = 0;
 constexpr int kCacheStream = 2;  // nt
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer access (gfx9 family)
