@@ -185,7 +185,8 @@ def main():
     kern_gbs = attn_bytes / (kern_us * 1e-6) / 1e9
     rows = wl.batch * wl.q_len
 
-    traffic = measured_traffic(args.traffic, wl.name)
+    kernel = attention_kernel(wl, x.max_kv_len)
+    traffic = measured_traffic(args.traffic, wl.name, kernel)
 
     sweep = None
     if args.sweep_splits:
@@ -386,7 +387,7 @@ def main():
             "algorithmic_bytes": acc_bytes,
         },
         "roofline": {
-            "kernel": "verify_attn_kernel",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": round(kern_gbs, 1),
             "peak": PEAK_HBM_GBS,
@@ -496,16 +497,31 @@ def ragged_round(x, wl, acc_in, page_table, stream, timed, n):
     return res
 
 
-def measured_traffic(path, workload):
-    """HBM bytes (FETCH + WRITE) per verify_attn launch from the rocprofv3
-    counter runs recorded under profiles/, or None when there is no record for
-    this workload or the kernel source has changed since it was taken."""
+def attention_kernel(wl, max_kv_len):
+    """The attention kernel the library's plan launches for this workload:
+    blocks of 49 to 96 rows per KV head with fp16 keys over a pass of 32 MB or
+    more (batch x KV heads x max_kv_len x 1 KB) take the two-half kernel, the
+    rest the row-tile kernel (the plan's rule, restated for the report)."""
+    rows = wl.q_len * (wl.num_q_heads // wl.num_kv_heads)
+    large = wl.batch * wl.num_kv_heads * max_kv_len * 2 * wl.head_dim * 2 >= 32 << 20
+    if wl.kv_dtype == "fp16" and 48 < rows <= 96 and large:
+        return "verify_rows_kernel"
+    return "verify_attn_kernel"
+
+
+def measured_traffic(path, workload, kernel):
+    """HBM bytes (FETCH + WRITE) per launch of the attention kernel from the
+    rocprofv3 counter runs recorded under profiles/, or None when there is no
+    record for this workload and kernel or the kernel's source has changed
+    since it was taken."""
     import hashlib
     path = path or os.path.join(ROOT, "profiles", f"traffic_verify_attn_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("kernel", "verify_attn_kernel") != kernel:
+        return None
     # the kernel's source files, hashed in the listed order as one byte string
     h = hashlib.sha256()
     for src in rec.get("sources") or [rec["source"]]:

@@ -61,6 +61,7 @@ struct Plan {
   bool claim;          // the keys of each (request, KV head) are claimed in grains (splits = slots per group)
   bool balanced;       // XCD-balanced static chunks (splits = slots per group, a multiple of 8)
   bool stream_once;    // one row tile and a large pass: the K/V copies go non-temporal
+  int halves;          // 2 or 3: the two-half kernel (verify_rows.hip) with that many row blocks per half
   size_t part_o_bytes, part_lse_bytes, ws_bytes;
 };
 
@@ -77,6 +78,10 @@ constexpr int kMinChunk = 128;         // tokens; below this the partial traffic
 // 32-request 8K-131K batch 8K-token chunks took 1,682 us at q=16 and 1,448 us
 // at q=8, 16K-token ones 1,638 and 1,437 us.
 constexpr int kBatchChunkCap = 16384;
+// the same for the two-half kernel, which holds 96 rows per workgroup: 8K
+// tokens (on the 32-request batch at q=16, 6K / 8K / 12K / 16K-token chunks
+// took 1,452 / 1,446 / 1,528 / 1,520 us)
+constexpr int kRowsBatchChunkCap = 8192;
 constexpr int kGroupsPerCU = 1;        // workgroups per CU the automatic plan aims at (LDS and registers allow one)
 
 sv_status validate(const sv_verify_params* p) {
@@ -137,6 +142,21 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     const long long whole = (maxkv + 15) / 16 * 16;
     maxkv = live < whole ? live : whole;
   }
+  // K/V bytes of the pass if every request were max_kv_len long (or its
+  // window): K and V rows of D channels, plus FP8's scale per 64 channels
+  const long long row_bytes = p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * (sv::kHeadDim + sv::kHeadDim / 64 * 2)
+                                                            : 2LL * sv::kHeadDim * 2;
+  const bool large = (long long)p->batch * p->num_kv_heads * maxkv * row_bytes >= sv::kStreamOnceBytes;
+  // 49 to 96 rows with fp16 keys over a large pass: one workgroup of two row
+  // halves reads each key once (verify_rows.hip) instead of two row tiles
+  // sharing it through L2; short passes keep the row tiles (a few rounds per
+  // chunk do not fill the two-half kernel's pipeline)
+  pl->halves = 0;
+  if (p->kv_dtype == SV_KV_FP16 && R > 48 && R <= 96 && large) {
+    pl->halves = R <= 64 ? 2 : 3;
+    pl->row_blocks = 1;
+    pl->rb = pl->halves;
+  }
   const long long rgs = pl->row_blocks;  // workgroups per (chunk, KV head, request)
   long long S;
   if (p->num_splits > 0) {
@@ -149,7 +169,8 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     const long long target = (long long)kGroupsPerCU * cu_count();
     S = (target + groups - 1) / groups;
     long long chunk = (maxkv + S - 1) / S;
-    const long long cap = p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * kBatchChunkCap : kBatchChunkCap;
+    const long long cap = pl->halves ? kRowsBatchChunkCap
+                          : p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * kBatchChunkCap : kBatchChunkCap;
     if (p->batch > 1 && chunk > cap) {
       // a whole multiple of the fill count keeps full rounds of workgroups
       S *= chunk / cap;
@@ -171,8 +192,19 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   long long chunk = (maxkv + S - 1) / S;
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
+  if (pl->halves && chunk > sv::kRowsMaxChunk) {
+    if (p->num_splits > 0) {
+      // a forced split count with longer chunks than the two-half kernel
+      // holds: the row tiles instead
+      pl->halves = 0;
+      pl->row_blocks = (rbt + 2) / 3;
+      pl->rb = (rbt + pl->row_blocks - 1) / pl->row_blocks;
+    } else {
+      chunk = sv::kRowsMaxChunk;
+    }
+  }
   S = (maxkv + chunk - 1) / chunk;
-  if (S * p->num_kv_heads * p->batch * 2 * rgs > 0x7fffffffLL)
+  if (S * p->num_kv_heads * p->batch * 2 * pl->row_blocks > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "too many workgroups (%lld splits)", S);
   // On request only (the rounding then varies between calls): one long
   // request with fp16 keys, full attention and one row tile, whose
@@ -184,7 +216,7 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   // chunks beats an equal number of workgroups per request.
   pl->claim = false;
   if ((p->options & SV_VERIFY_CLAIMED_WORK) && p->batch == 1 && p->window == 0 && p->kv_dtype == SV_KV_FP16 &&
-      pl->row_blocks == 1 && p->num_kv_heads <= sv::kCounterSlots) {
+      pl->row_blocks == 1 && pl->halves == 0 && p->num_kv_heads <= sv::kCounterSlots) {
     const long long S8 = p->num_splits > 0 ? S : (S + 7) / 8 * 8;
     if (S8 >= 8 && S8 % 8 == 0 && (maxkv + 15) / 16 >= 64LL * sv::kWavesPerGroup * S8) {
       S = S8;
@@ -199,7 +231,7 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   // reproducible bits. Each request's chunks follow its own length, so a
   // ragged batch of this size still ends with its longest request's slots.
   pl->balanced = false;
-  if (!pl->claim && p->window == 0 && pl->row_blocks == 1 && p->kv_dtype == SV_KV_FP16) {
+  if (!pl->claim && p->window == 0 && pl->row_blocks == 1 && pl->halves == 0 && p->kv_dtype == SV_KV_FP16) {
     const long long S8 = p->num_splits > 0 ? S : (S + 7) / 8 * 8;
     if (S8 >= 8 && S8 % 8 == 0 && (maxkv + 15) / 16 >= 64LL * sv::kWavesPerGroup * S8 &&
         (long long)p->batch * p->num_kv_heads * S8 <= cu_count()) {
@@ -209,12 +241,7 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
   }
   pl->splits = (int)S;
   pl->chunk = (int)chunk;
-  // K/V bytes of the pass if every request were max_kv_len long (or its
-  // window): K and V rows of D channels, plus FP8's scale per 64 channels
-  const long long row_bytes = p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * (sv::kHeadDim + sv::kHeadDim / 64 * 2)
-                                                            : 2LL * sv::kHeadDim * 2;
-  pl->stream_once = pl->row_blocks == 1 &&
-                    (long long)p->batch * p->num_kv_heads * maxkv * row_bytes >= sv::kStreamOnceBytes;
+  pl->stream_once = pl->row_blocks == 1 && large;
   if (S > 1) {
     const size_t rows = (size_t)p->batch * p->q_len * p->num_q_heads;
     pl->part_o_bytes = align256((size_t)S * rows * sv::kHeadDim * sizeof(float));
@@ -311,7 +338,10 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.window = p->window;
   a.sink = p->sink;
   a.balanced = (pl.balanced && !q_start) ? 1 : 0;
-  sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, claim, pl.stream_once, s);
+  if (pl.halves)
+    sv::launch_verify_rows(a, pl.halves, s);
+  else
+    sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, claim, pl.stream_once, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
   if (pl.splits > 1) {

@@ -191,6 +191,12 @@ __host__ __device__ inline int xcd_chunk_start(int total, int s, int S) {
 }
 
 void launch_verify_attention(const AttnArgs& a, int rb, bool fp8, bool claim, bool stream_once, hipStream_t s);
+// 49 to 96 rows per KV head, fp16 keys, a large pass (verify_rows.hip): one
+// workgroup per (chunk, KV head, request), rb row blocks per half; chunks of
+// at most kRowsMaxChunk tokens (the workgroup keeps the chunk's cache rows in
+// LDS)
+void launch_verify_rows(const AttnArgs& a, int rb, hipStream_t s);
+constexpr int kRowsMaxChunk = 32768;
 void launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace sv

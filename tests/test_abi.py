@@ -272,7 +272,7 @@ def test_noalloc_entry_point_refuses_plans_beyond_its_scratch():
     (1, 8, 4104, 16, B.SV_KV_FP16, 33),            # 4K: chunks of 128 (the smallest)
     (8, 8, 32776, 16, B.SV_KV_FP16, 8),            # 8 x 32K: one round, XCD-balanced
     (1, 8, 524296, 16, B.SV_KV_FP16, 64),          # 512K: one workgroup per CU, XCD-balanced
-    (32, 16, 131088, 64, B.SV_KV_FP16, 8),         # ragged q=16 bound: 16K-token chunk cap
+    (32, 16, 131088, 64, B.SV_KV_FP16, 16),        # ragged q=16 bound: the two-half kernel's 8K-token cap
     (4, 8, 262152, 16, B.SV_KV_FP8_E4M3, 16),      # FP8 4 x 262K: one workgroup per CU (under its 32K cap)
 ])
 def test_plans_of_the_benchmark_workloads(batch, q_len, max_kv, page, dtype, splits):
