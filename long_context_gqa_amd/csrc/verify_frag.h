@@ -451,12 +451,24 @@ __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t r, char* ring, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SV_LP(ring + (J & 4) * 1024), 16, lane_off, J >= 4 ? 4096 : 0,
                                            (J & 3) * 1024, CP);
 }
+// Per-lane byte offsets of the copies of the blocks with even and odd index
+// j (lane l copies 16-byte chunk c = l % 32 of token t = 2j + l / 32). K: the
+// chunk lands at chunk c ^ (t & 3); V: at c ^ 2 (t & 3).
+__device__ __forceinline__ void k_copy_offsets(int lane, uint32_t* even, uint32_t* odd) {
+  const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
+  *even = h * 512u + 16u * (c ^ h);
+  *odd = h * 512u + 16u * (c ^ (2u + h));
+}
+__device__ __forceinline__ void v_copy_offsets(int lane, uint32_t* even, uint32_t* odd) {
+  const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
+  *even = h * 512u + 16u * (c ^ (2u * h));
+  *odd = h * 512u + 16u * (c ^ (4u + 2u * h));
+}
 template <int B0, int B1, int CP>
 __device__ __forceinline__ void dma_k(const _Float16* kb, char* ring, int lane) {
   const __amdgpu_buffer_rsrc_t r = half_step_rsrc(kb);
-  const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
-  // token t = 2j + h of block j, 16-byte chunk c at chunk c ^ (t & 3)
-  const uint32_t even = h * 512u + 16u * (c ^ h), odd = h * 512u + 16u * (c ^ (2u + h));
+  uint32_t even, odd;
+  k_copy_offsets(lane, &even, &odd);
   if constexpr (B0 <= 0 && 0 < B1) dma_block<0, CP>(r, ring, even);
   if constexpr (B0 <= 1 && 1 < B1) dma_block<1, CP>(r, ring, odd);
   if constexpr (B0 <= 2 && 2 < B1) dma_block<2, CP>(r, ring, even);
@@ -469,9 +481,8 @@ __device__ __forceinline__ void dma_k(const _Float16* kb, char* ring, int lane) 
 template <int B0, int B1, int CP>
 __device__ __forceinline__ void dma_v(const _Float16* vb, char* ring, int lane) {
   const __amdgpu_buffer_rsrc_t r = half_step_rsrc(vb);
-  const uint32_t h = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
-  // token t = 2j + h of block j, 16-byte chunk c at chunk c ^ 2 (t & 3)
-  const uint32_t even = h * 512u + 16u * (c ^ (2u * h)), odd = h * 512u + 16u * (c ^ (4u + 2u * h));
+  uint32_t even, odd;
+  v_copy_offsets(lane, &even, &odd);
   if constexpr (B0 <= 0 && 0 < B1) dma_block<0, CP>(r, ring, even);
   if constexpr (B0 <= 1 && 1 < B1) dma_block<1, CP>(r, ring, odd);
   if constexpr (B0 <= 2 && 2 < B1) dma_block<2, CP>(r, ring, even);

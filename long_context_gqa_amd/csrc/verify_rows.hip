@@ -17,10 +17,11 @@
 // (the matrix op sums over the k-slots in any order).
 //
 // The two waves of a row half share one online-softmax reference per row:
-// each publishes its step's row maxima, and in the next round both take the
-// same decision from both maxima (the lazy rule of verify_attn_kernel), so
-// their P^T fragments are at one reference and their O^T halves and sums
-// need no rescale when combined. Pipeline: the scores of round q, the
+// each publishes its lanes' maxima of its step (4 tokens a lane), and in the
+// next round each lane tests its own maximum with the partner's of the same
+// lane, so both waves see the same values and take the same decision (the
+// lazy rule of verify_attn_kernel); their P^T fragments are then at one
+// reference, and their O^T halves and sums need no rescale when combined. Pipeline: the scores of round q, the
 // reference and P of round q - 1, and the PV of round q - 2 run in round q.
 // K and V pass through rings that all four waves share (K: 3 rounds, V: 5),
 // two rounds in flight; each wave issues the copies of one half-step (K or V
@@ -112,14 +113,14 @@ __device__ __forceinline__ void clear_tail(u32x2 (&v)[8], int lane, int t0, int 
   }
 }
 
-// The copies of one half-step, K (is_v false: dma_k's swizzle) or V (dma_v's),
+// The copies of one half-step, K (is_v false: dma_k's layout) or V (dma_v's),
 // with the lane offsets selected rather than branched on.
 template <int CP>
 __device__ __forceinline__ void dma_half(const _Float16* base, char* ring, int lane, bool is_v) {
   const __amdgpu_buffer_rsrc_t r = half_step_rsrc(base);
-  const uint32_t hh = (uint32_t)lane >> 5, c = (uint32_t)lane & 31u;
-  const uint32_t ek = hh * 512u + 16u * (c ^ hh), ok = hh * 512u + 16u * (c ^ (2u + hh));
-  const uint32_t ev = hh * 512u + 16u * (c ^ (2u * hh)), ov = hh * 512u + 16u * (c ^ (4u + 2u * hh));
+  uint32_t ek, ok, ev, ov;
+  k_copy_offsets(lane, &ek, &ok);
+  v_copy_offsets(lane, &ev, &ov);
   const uint32_t even = is_v ? ev : ek, odd = is_v ? ov : ok;
   dma_block<0, CP>(r, ring, even);
   dma_block<1, CP>(r, ring, odd);
