@@ -258,8 +258,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 }
 
 // One wave per (row, head), for launches with many items (each with few
-// splits): wave reductions only, no workgroup barriers. Each lane owns a
-// float4 of channels and keeps four splits' loads in flight.
+// splits): no workgroup barriers. Each lane owns a float4 of channels; up to
+// 16 splits are loaded at once, more four at a time with wave reductions of
+// the lse values.
 __global__ __launch_bounds__(kThreads) void merge_wave_kernel(MergeArgs a) {
   settle_counters(a);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -272,6 +273,44 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(MergeArgs a) {
   const size_t so = sl * a.head_dim;
   const float* lse = a.part_lse + item;
   const float* po = a.part_o + item * a.head_dim;
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  // Up to 16 splits of 256 channels: every lane loads its float4 of all
+  // splits and every split's lse at once (one round trip), then reduces in
+  // registers.
+  constexpr int kOnce = 16;
+  if (S <= kOnce && a.head_dim == 4 * kWave) {
+    float lv[kOnce];
+    float4 ov[kOnce];
+#pragma unroll
+    for (int s = 0; s < kOnce; ++s) {
+      lv[s] = -INFINITY;
+      ov[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < S) {
+        lv[s] = lse[s * sl];
+        ov[s] = reinterpret_cast<const float4*>(po + s * so)[lane];
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kOnce; ++s) M = fmaxf(M, lv[s]);
+    const float ref = (M == -INFINITY) ? 0.f : M;
+    float t = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < kOnce; ++s) {
+      const float wgt = (lv[s] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((lv[s] - ref) * kLog2e);
+      t += wgt;
+      acc.x += wgt * ov[s].x;
+      acc.y += wgt * ov[s].y;
+      acc.z += wgt * ov[s].z;
+      acc.w += wgt * ov[s].w;
+    }
+    const float inv = t > 0.f ? 1.f / t : 0.f;
+    h4 hv = {(_Float16)(acc.x * inv), (_Float16)(acc.y * inv), (_Float16)(acc.z * inv), (_Float16)(acc.w * inv)};
+    reinterpret_cast<h4*>(a.out + item * a.head_dim)[lane] = hv;
+    if (a.out_lse && lane == 0) a.out_lse[item] = t > 0.f ? ref + __builtin_amdgcn_logf(t) * kLn2 : -INFINITY;
+    return;
+  }
   float mx = -INFINITY;
   for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, lse[s * sl]);
   mx = wave_max(mx);
@@ -313,7 +352,6 @@ __global__ __launch_bounds__(kThreads) void merge_wave_kernel(MergeArgs a) {
       acc.z += wgt * o.z;
       acc.w += wgt * o.w;
     }
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     h4 hv = {(_Float16)(acc.x * inv), (_Float16)(acc.y * inv), (_Float16)(acc.z * inv), (_Float16)(acc.w * inv)};
     reinterpret_cast<h4*>(a.out + item * a.head_dim)[d4] = hv;
   }
