@@ -5,8 +5,8 @@ that): blocks of q = 9..16 at 6 query heads per KV head (54..96 rows, halves
 of 32 or 48 rows) and q = 8, 12 at 8, automatic and forced split counts
 (chunks of odd and even step counts, and chunks of 2 to 8 steps, where only
 the pipeline's first and last rounds run), pages of 16 to 64 positions, a
-sliding window, blocks of a width per request, and repeated and
-page-permuted calls that must give the same bits."""
+sliding window, blocks of a width per request, a request whose rows see no
+key, and repeated and page-permuted calls that must give the same bits."""
 import numpy as np
 import pytest
 import torch
@@ -110,3 +110,25 @@ def test_halves_repeat_and_page_permutation_bitwise():
     x2.page_table = t
     out2, lse2, _ = run_gpu(x2)
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_halves_request_with_rows_but_no_visible_key():
+    # kv_len 0 for request 1 (below its block of 16): its rows get 0 and -inf
+    # and the flag (its chunk has no step: only the pipeline's edge rounds
+    # run); every other request matches the oracle
+    lens, q = [4200, 900, 4133, 2500], 16
+    assert large(len(lens), 4, max(lens))
+    x = case(len(lens), q, lens, 16, "unit", seed=97)
+    kv = x.kv_lens.clone()
+    kv[1] = 0
+    for splits in (0, 1, 3):
+        say(f"no visible key, splits={splits}")
+        out, lse, flags = run_gpu(x, num_splits=splits, kv_lens=kv, max_kv_len=max(lens))
+        assert flags & 2
+        assert (out[q:2 * q] == 0).all() and np.isneginf(lse[q:2 * q]).all()
+        h = host(x)
+        keep = [b for b in range(len(lens)) if b != 1]
+        ref, ref_lse = oatt.verify_attention(h["q"], h["k_pages"], h["v_pages"], h["page_table"], h["kv_lens"], q,
+                                             x.sm_scale, rows=[(b, g) for b in keep for g in range(4)])
+        rows = np.concatenate([np.arange(b * q, (b + 1) * q) for b in keep])
+        check(out[rows], lse[rows], ref[rows], ref_lse[rows], what=f"other requests, splits={splits}")
