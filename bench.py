@@ -185,7 +185,7 @@ def main():
     kern_gbs = attn_bytes / (kern_us * 1e-6) / 1e9
     rows = wl.batch * wl.q_len
 
-    kernel = attention_kernel(wl, x.max_kv_len)
+    kernel = "verify_rows_kernel" if call.kernel == B.SV_KERNEL_TWO_HALVES else "verify_attn_kernel"
     traffic = measured_traffic(args.traffic, wl.name, kernel)
 
     sweep = None
@@ -495,18 +495,6 @@ def ragged_round(x, wl, acc_in, page_table, stream, timed, n):
     log(f"[bench] ragged round: {rows} rows; prepare {res['prepare_us']} us, append {res.get('append_us')} us, "
         f"verify {res['verify_us']} us ({res['verify_GBps']} GB/s), accept {res['accept_us']} us")
     return res
-
-
-def attention_kernel(wl, max_kv_len):
-    """The attention kernel the library's plan launches for this workload:
-    blocks of 49 to 96 rows per KV head with fp16 keys over a pass of 32 MB or
-    more (batch x KV heads x max_kv_len x 1 KB) take the two-half kernel, the
-    rest the row-tile kernel (the plan's rule, restated for the report)."""
-    rows = wl.q_len * (wl.num_q_heads // wl.num_kv_heads)
-    large = wl.batch * wl.num_kv_heads * max_kv_len * 2 * wl.head_dim * 2 >= 32 << 20
-    if wl.kv_dtype == "fp16" and 48 < rows <= 96 and large:
-        return "verify_rows_kernel"
-    return "verify_attn_kernel"
 
 
 def measured_traffic(path, workload, kernel):

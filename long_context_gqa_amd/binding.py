@@ -29,7 +29,9 @@ EXPORTED = (
     "sv_rejection_accept_workspace_bytes",
     "sv_rejection_accept", "sv_topk_candidates_workspace_bytes", "sv_topk_candidates", "sv_status_string",
     "sv_last_error", "sv_version", "sv_verify_scratch_bytes", "sv_verify_attention_noalloc",
+    "sv_verify_plan_kernel",
 )
+SV_KERNEL_ROW_TILES, SV_KERNEL_TWO_HALVES = 0, 1
 
 
 class SvError(RuntimeError):
@@ -74,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.sv_verify_workspace_bytes.restype = sz
         L.sv_verify_plan.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.sv_verify_plan.restype = ctypes.c_int
+        L.sv_verify_plan_kernel.argtypes = [P, ctypes.POINTER(i32)]
+        L.sv_verify_plan_kernel.restype = ctypes.c_int
         L.sv_verify_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, f32p, vp, sz, vp, vp]
         L.sv_verify_attention.restype = ctypes.c_int
         L.sv_verify_scratch_bytes.argtypes = []
@@ -157,6 +161,13 @@ def sv_verify_plan(p: SvVerifyParams) -> tuple[int, int]:
     s, c = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().sv_verify_plan(ctypes.byref(p), ctypes.byref(s), ctypes.byref(c)))
     return s.value, c.value
+
+
+def sv_verify_plan_kernel(p: SvVerifyParams) -> int:
+    """SV_KERNEL_ROW_TILES or SV_KERNEL_TWO_HALVES: the kernel the plan launches."""
+    k = ctypes.c_int32()
+    _check(lib().sv_verify_plan_kernel(ctypes.byref(p), ctypes.byref(k)))
+    return k.value
 
 
 def sv_verify_attention(p: SvVerifyParams, q, k_pages, v_pages, k_scales, v_scales, page_table, kv_lens,
@@ -298,6 +309,7 @@ class VerifyCall:
         self.workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
         self.splits, self.chunk = sv_verify_plan(self.params)
+        self.kernel = sv_verify_plan_kernel(self.params)
 
     def run(self, stream=None):
         sv_verify_attention(self.params, *self.inputs, self.out, self.out_lse, self.workspace, self.flags,
@@ -367,6 +379,7 @@ class RaggedVerifyCall:
         self.workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
         self.splits, self.chunk = sv_verify_plan(self.params)
+        self.kernel = sv_verify_plan_kernel(self.params)
 
     def run(self, stream=None):
         sv_verify_attention_ragged(self.params, self.q_start, *self.inputs, self.out, self.out_lse, self.workspace,

@@ -82,6 +82,13 @@ constexpr int kBatchChunkCap = 16384;
 // tokens (on the 32-request batch at q=16, 6K / 8K / 12K / 16K-token chunks
 // took 1,452 / 1,446 / 1,528 / 1,520 us)
 constexpr int kRowsBatchChunkCap = 8192;
+// shortest automatic chunk for the two-half kernel: its pipeline takes five
+// edge rounds per chunk, and below this the row tiles are faster (one
+// request at q = 16 over 8K / 20K / 65K / 131K positions: 39.4 / 46.6 / 72.4
+// / 124 us with chunks of 192 / 320 / 1,024 / 2,048 tokens, against 33.3 /
+// 40.0 / 65.7 / 128.9 us with the row tiles; four requests of 16.5K with
+// 1,088-token chunks: 76.2 against 67.5 us)
+constexpr int kRowsMinChunk = 2048;
 constexpr int kGroupsPerCU = 1;        // workgroups per CU the automatic plan aims at (LDS and registers allow one)
 
 sv_status validate(const sv_verify_params* p) {
@@ -157,50 +164,65 @@ sv_status make_plan(const sv_verify_params* p, Plan* pl) {
     pl->row_blocks = 1;
     pl->rb = pl->halves;
   }
-  const long long rgs = pl->row_blocks;  // workgroups per (chunk, KV head, request)
-  long long S;
-  if (p->num_splits > 0) {
-    S = p->num_splits;
-  } else {
-    // Enough chunks for one workgroup per CU when every request is as long as
-    // max_kv_len; for batches (whose lengths may be ragged) also cap the chunk
-    // so that the work is cut into pieces small enough to balance.
-    const long long groups = (long long)p->batch * p->num_kv_heads * rgs;
-    const long long target = (long long)kGroupsPerCU * cu_count();
-    S = (target + groups - 1) / groups;
-    long long chunk = (maxkv + S - 1) / S;
-    const long long cap = pl->halves ? kRowsBatchChunkCap
-                          : p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * kBatchChunkCap : kBatchChunkCap;
-    if (p->batch > 1 && chunk > cap) {
-      // a whole multiple of the fill count keeps full rounds of workgroups
-      S *= chunk / cap;
-      chunk = (maxkv + S - 1) / S;
-    }
-    if (chunk < kMinChunk) chunk = kMinChunk;
-    S = (maxkv + chunk - 1) / chunk;
-    if (S < 1) S = 1;
-    if (rgs > 1) {
-      // the row tiles of a unit all run on the unit's XCD (unit mod 8), so a
-      // unit count that is a multiple of 8 spreads the work over every XCD
-      const long long hb = (long long)p->batch * p->num_kv_heads;
-      long long need = 8;
-      while (need > 1 && hb % (8 / need * 2) == 0) need /= 2;  // 8 / gcd(8, hb)
-      const long long S8 = (S + need - 1) / need * need;
-      if (maxkv >= S8 * kMinChunk) S = S8;
-    }
-  }
-  long long chunk = (maxkv + S - 1) / S;
-  chunk = (chunk + 63) / 64 * 64;
-  if (chunk < 64) chunk = 64;
-  if (pl->halves && chunk > sv::kRowsMaxChunk) {
+  // split count and chunk length for the kernel chosen so far
+  auto size_splits = [&](long long* S_out, long long* chunk_out) {
+    const long long rgs = pl->row_blocks;  // workgroups per (chunk, KV head, request)
+    long long S;
     if (p->num_splits > 0) {
-      // a forced split count with longer chunks than the two-half kernel
-      // holds: the row tiles instead
-      pl->halves = 0;
-      pl->row_blocks = (rbt + 2) / 3;
-      pl->rb = (rbt + pl->row_blocks - 1) / pl->row_blocks;
+      S = p->num_splits;
     } else {
+      // Enough chunks for one workgroup per CU when every request is as long
+      // as max_kv_len; for batches (whose lengths may be ragged) also cap the
+      // chunk so that the work is cut into pieces small enough to balance.
+      const long long groups = (long long)p->batch * p->num_kv_heads * rgs;
+      const long long target = (long long)kGroupsPerCU * cu_count();
+      S = (target + groups - 1) / groups;
+      long long chunk = (maxkv + S - 1) / S;
+      const long long cap = pl->halves ? kRowsBatchChunkCap
+                            : p->kv_dtype == SV_KV_FP8_E4M3 ? 2LL * kBatchChunkCap : kBatchChunkCap;
+      if (p->batch > 1 && chunk > cap) {
+        // a whole multiple of the fill count keeps full rounds of workgroups
+        S *= chunk / cap;
+        chunk = (maxkv + S - 1) / S;
+      }
+      if (chunk < kMinChunk) chunk = kMinChunk;
+      S = (maxkv + chunk - 1) / chunk;
+      if (S < 1) S = 1;
+      if (rgs > 1) {
+        // the row tiles of a unit all run on the unit's XCD (unit mod 8), so a
+        // unit count that is a multiple of 8 spreads the work over every XCD
+        const long long hb = (long long)p->batch * p->num_kv_heads;
+        long long need = 8;
+        while (need > 1 && hb % (8 / need * 2) == 0) need /= 2;  // 8 / gcd(8, hb)
+        const long long S8 = (S + need - 1) / need * need;
+        if (maxkv >= S8 * kMinChunk) S = S8;
+      }
+    }
+    long long chunk = (maxkv + S - 1) / S;
+    chunk = (chunk + 63) / 64 * 64;
+    if (chunk < 64) chunk = 64;
+    *S_out = S;
+    *chunk_out = chunk;
+  };
+  auto use_row_tiles = [&]() {
+    pl->halves = 0;
+    pl->row_blocks = (rbt + 2) / 3;
+    pl->rb = (rbt + pl->row_blocks - 1) / pl->row_blocks;
+  };
+  long long S, chunk;
+  size_splits(&S, &chunk);
+  if (pl->halves && p->num_splits > 0 && chunk > sv::kRowsMaxChunk) {
+    // a forced split count with longer chunks than the two-half kernel
+    // holds: the row tiles instead
+    use_row_tiles();
+    size_splits(&S, &chunk);
+  } else if (pl->halves && p->num_splits == 0) {
+    if (chunk > sv::kRowsMaxChunk) {
       chunk = sv::kRowsMaxChunk;
+    } else if (chunk < kRowsMinChunk) {
+      // too short for the two-half kernel's pipeline
+      use_row_tiles();
+      size_splits(&S, &chunk);
     }
   }
   S = (maxkv + chunk - 1) / chunk;
@@ -270,6 +292,15 @@ sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t
   if (st != SV_OK) return st;
   if (num_splits) *num_splits = pl.splits;
   if (chunk_tokens) *chunk_tokens = pl.chunk;
+  return ok();
+}
+
+sv_status sv_verify_plan_kernel(const sv_verify_params* p, int32_t* kernel) {
+  if (!kernel) return fail(SV_ERR_INVALID_ARGUMENT, "kernel is NULL");
+  Plan pl;
+  sv_status st = make_plan(p, &pl);
+  if (st != SV_OK) return st;
+  *kernel = pl.halves ? SV_KERNEL_TWO_HALVES : SV_KERNEL_ROW_TILES;
   return ok();
 }
 

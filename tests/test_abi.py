@@ -284,3 +284,40 @@ def test_plans_of_the_benchmark_workloads(batch, q_len, max_kv, page, dtype, spl
     s, c = B.sv_verify_plan(p)
     assert s == splits, (s, c)
     assert c % 64 == 0 and s * c >= max_kv
+
+
+@pytest.mark.parametrize("batch,q_len,max_kv,page,dtype,splits,kernel", [
+    # 96 rows per KV head, fp16, automatic splits: the two-half kernel only
+    # where its chunks are at least 2,048 positions long
+    (1, 16, 13000, 16, B.SV_KV_FP16, 0, B.SV_KERNEL_ROW_TILES),     # 53 MB, chunks of 256 for the halves
+    (1, 16, 65000, 16, B.SV_KV_FP16, 0, B.SV_KERNEL_ROW_TILES),     # chunks of 1,024 for the halves
+    (4, 16, 16500, 16, B.SV_KV_FP16, 0, B.SV_KERNEL_ROW_TILES),     # chunks of 1,088 for the halves
+    (1, 16, 131000, 16, B.SV_KV_FP16, 0, B.SV_KERNEL_TWO_HALVES),   # chunks of 2,048
+    (8, 16, 32776, 16, B.SV_KV_FP16, 0, B.SV_KERNEL_TWO_HALVES),
+    (32, 16, 131088, 64, B.SV_KV_FP16, 0, B.SV_KERNEL_TWO_HALVES),  # the ragged batch's bound: 8K-token chunks
+    (1, 16, 524296, 16, B.SV_KV_FP16, 0, B.SV_KERNEL_TWO_HALVES),
+    # forced splits keep it down to the shortest chunks (tests of the pipeline's edge rounds)
+    (2, 16, 4200, 16, B.SV_KV_FP16, 33, B.SV_KERNEL_TWO_HALVES),
+    (1, 16, 13000, 16, B.SV_KV_FP16, 5, B.SV_KERNEL_TWO_HALVES),
+    # under 32 MB, at most 48 rows, FP8 keys, or chunks beyond 32,768: row tiles
+    (2, 16, 3000, 16, B.SV_KV_FP16, 33, B.SV_KERNEL_ROW_TILES),
+    (1, 8, 524296, 16, B.SV_KV_FP16, 0, B.SV_KERNEL_ROW_TILES),
+    (1, 16, 524296, 16, B.SV_KV_FP8_E4M3, 0, B.SV_KERNEL_ROW_TILES),
+    (1, 16, 131000, 16, B.SV_KV_FP16, 2, B.SV_KERNEL_ROW_TILES),
+])
+def test_plan_kernel_choice(batch, q_len, max_kv, page, dtype, splits, kernel):
+    pages = -(-max_kv // page)
+    p = _p(batch=batch, q_len=q_len, page_size=page, max_kv_len=max_kv, max_pages_per_req=pages,
+           num_pages=pages * batch, kv_dtype=dtype, num_splits=splits)
+    assert B.sv_verify_plan_kernel(p) == kernel
+    if kernel == B.SV_KERNEL_TWO_HALVES:
+        s, c = B.sv_verify_plan(p)
+        assert c <= 32768 and (splits > 0 or c >= 2048), (s, c)
+
+
+def test_plan_kernel_rejects_null_and_bad_shapes():
+    lib = B.lib()
+    assert lib.sv_verify_plan_kernel(ctypes.byref(_p()), None) == B.SV_ERR_INVALID_ARGUMENT
+    k = ctypes.c_int32(-1)
+    assert lib.sv_verify_plan_kernel(ctypes.byref(_p(head_dim=128)), ctypes.byref(k)) == B.SV_ERR_UNSUPPORTED
+    assert k.value == -1

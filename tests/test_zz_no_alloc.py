@@ -2,8 +2,9 @@
 workspace in the library's own device scratch) against sv_verify_attention
 with a caller workspace, through the C ABI: the same plan and kernels, so the
 same bits, on calls in a row over shrinking inputs (the 512K single request,
-a 40K request on 8 XCD-balanced splits, a 13K request at q = 16 on the
-two-half kernel, automatic and forced splits, a batch of two 6K requests), and the
+a 131K request at q = 16 on the two-half kernel, a 40K request on 8
+XCD-balanced splits, a 12K request at q = 16 on the two-half kernel with
+forced splits, a batch of two 6K requests), and the
 claimed-work option, whose counters live at the start of the scratch (zero
 at load, left zero by every call)."""
 import numpy as np
@@ -40,14 +41,19 @@ def both(x, splits=0, claim=False, max_kv=None):
 
 
 def test_noalloc_matches_the_workspace_call_on_shrinking_inputs():
-    cases = [("512K", lambda: W.make_verify_inputs(W.WORKLOADS[3], "unit", device="cuda"), 0),
-             ("40K, 8 splits", lambda: case(1, 8, [40003], 16, "unit", seed=5), 8),
-             # a 53 MB pass of 96 rows per KV head: the two-half kernel
-             ("13K at q=16", lambda: case(1, 16, [13000], 16, "unit", seed=8), 0),
-             ("12K at q=16, 5 splits", lambda: case(1, 16, [12001], 16, "unit", seed=9), 5),
-             ("2 x 6K", lambda: case(2, 8, [6000, 5100], 16, "unit", seed=6), 0)]
-    for name, make, splits in cases:
+    # (the 131K and 12K blocks of 96 rows per KV head run on the two-half kernel)
+    cases = [("512K", lambda: W.make_verify_inputs(W.WORKLOADS[3], "unit", device="cuda"), 0, None),
+             ("131K at q=16", lambda: case(1, 16, [131000], 16, "unit", seed=8), 0, B.SV_KERNEL_TWO_HALVES),
+             ("40K, 8 splits", lambda: case(1, 8, [40003], 16, "unit", seed=5), 8, None),
+             ("12K at q=16, 5 splits", lambda: case(1, 16, [12001], 16, "unit", seed=9), 5, B.SV_KERNEL_TWO_HALVES),
+             ("2 x 6K", lambda: case(2, 8, [6000, 5100], 16, "unit", seed=6), 0, None)]
+    for name, make, splits, kernel in cases:
         x = make()
+        if kernel is not None:
+            c = B.VerifyCall(x.q, x.k_pages, x.v_pages, x.page_table.cuda(), x.kv_lens.cuda(), x.wl.q_len,
+                             int(x.kv_lens.max()), None, None, x.sm_scale, splits)
+            assert c.kernel == kernel
+            del c
         (o1, l1, f1), (o2, l2, f2) = both(x, splits)
         say(f"{name}: bitwise equal {torch.equal(o1, o2) and torch.equal(l1, l2)}")
         assert f1 == 0 and f2 == 0
