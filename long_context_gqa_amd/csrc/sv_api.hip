@@ -369,9 +369,13 @@ sv_status verify_attention_impl(const sv_verify_params* p, const int32_t* q_star
   a.window = p->window;
   a.sink = p->sink;
   a.balanced = (pl.balanced && !q_start) ? 1 : 0;
-  if (pl.halves)
+  if (pl.halves) {
+    // (the plan keeps these by construction; the kernel's tables rely on them)
+    if (pl.chunk > sv::kRowsMaxChunk || pl.chunk % 64 != 0 || p->q_len * a.group > 32 * pl.halves)
+      return fail(SV_ERR_UNSUPPORTED, "internal plan error: two-half kernel with chunk %d, %d rows", pl.chunk,
+                  p->q_len * a.group);
     sv::launch_verify_rows(a, pl.halves, s);
-  else
+  } else
     sv::launch_verify_attention(a, pl.rb, p->kv_dtype == SV_KV_FP8_E4M3, claim, pl.stream_once, s);
   st = check_launch("verify_attn");
   if (st != SV_OK) return st;
