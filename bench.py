@@ -82,8 +82,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the verify path is measured on a "
-                                   "single MI355X; run with --gpus 1"}))
+        print(json.dumps({"error": "the verify path runs and is measured on one GPU (one MI355X); "
+                                   "run with --gpus 1"}))
         sys.exit(2)
 
     import numpy as np
