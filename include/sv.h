@@ -131,18 +131,20 @@ size_t sv_verify_workspace_bytes(const sv_verify_params* p);
 sv_status sv_verify_plan(const sv_verify_params* p, int32_t* num_splits, int32_t* chunk_tokens);
 
 /*
- * The attention kernel the planner launches for these parameters (the
- * arithmetic is the same; the kernels differ in how a workgroup covers the
- * rows of a KV head):
+ * The attention kernel the planner launches for these parameters (both
+ * compute the same attention, equal to rounding; they differ in how a
+ * workgroup covers the rows of a KV head):
  *   SV_KERNEL_ROW_TILES   up to 48 rows per workgroup; more rows as row tiles
  *                         (workgroups on the same keys, shared through L2)
  *   SV_KERNEL_TWO_HALVES  49 to 96 rows in one workgroup of two row halves
  *                         that split the output channels; taken for fp16
  *                         keys over a pass of 32 MB or more (batch x KV
- *                         heads x max_kv_len x 1 KB) whose chunks are at
+ *                         heads x max_kv_len x 1 KB; with a window, its
+ *                         span instead of max_kv_len) whose chunks are at
  *                         least 2,048 positions long (any length up to 32,768
  *                         when num_splits is forced)
- * Host only; the status is that of the plan (as for sv_verify_plan).
+ * Host only; the status is that of the plan (as for sv_verify_plan), and
+ * SV_ERR_INVALID_ARGUMENT for a NULL `kernel`.
  */
 typedef enum { SV_KERNEL_ROW_TILES = 0, SV_KERNEL_TWO_HALVES = 1 } sv_verify_kernel;
 sv_status sv_verify_plan_kernel(const sv_verify_params* p, int32_t* kernel);
